@@ -1,0 +1,188 @@
+#!/usr/bin/env python
+"""Benchmark of the exact-attention path on one MI355X; prints ONE JSON line.
+
+A step is one pass of the whole path over resident synthetic inputs:
+  1. fa_fwd    B=1 H=32 N=8192 d=128 bf16, causal, Q scaled x2
+  2. fa_bwd    the same shape (dO ~ N(0,1)), consuming the forward's O and lse
+  3. fa_decode B=64 H=32 Nkv=16384 d=128 bf16, 16 history chunks per head
+value = (fwd + bwd useful FLOPs) / (fwd + bwd time), in TFLOP/s, with
+useful FLOPs 4 B H N^2 d (forward) and 10 B H N^2 d (backward: five N x N x d
+products), both halved for the causal mask.  Decode is reported in GB/s of
+algorithmic HBM bytes (K + V + q + o).  Each entry point is timed live with
+HIP events recorded on the stream its kernels run on (torch's current
+stream, which the binding hands to the library).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+CSRC = os.path.join(ROOT, "exact_io_aware_31_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "bwd": "fa_bwd.hip", "decode": "fa_decode.hip"}
+
+
+def source_sha(entry: str) -> str:
+    with open(os.path.join(CSRC, KERNEL_SOURCES[entry]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(entry: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if the kernel is unchanged since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        kv = dict(tok.split("=", 1) for tok in line.split() if "=" in tok)
+        if kv.get("entry") == entry:
+            if kv.get("source_sha256") != source_sha(entry):
+                return None
+            return float(kv["bytes_per_launch"])
+    return None
+
+
+def cpu_baseline(q, k, v, do, lse_unused, decode_inputs, heads: int, scale: float):
+    """The float64 oracle, unmodified, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+
+    n, d = q.shape[-2], q.shape[-1]
+    t0 = time.perf_counter()
+    for h in range(heads):
+        qh, kh, vh, doh = (t[0, h].cpu() for t in (q, k, v, do))
+        oracle.attn_fwd(qh, kh, vh, scale, True)
+        oracle.attn_bwd(qh, kh, vh, doh, scale, True)
+    secs = time.perf_counter() - t0
+    flops = heads * (4 + 10) * n * n * d / 2
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"float64 oracle forward + backward on {heads} of 32 heads of the "
+                      f"N={n} d={d} causal workload ({secs:.1f} s; useful-FLOP formula)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this attention path runs on a single GPU "
+              "(attention heads are independent, so N GPUs would each run their own share "
+              "with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_31_amd as fa
+    from synth_inputs import DECODE_16K, FWD_8K, attention_inputs
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w, wd = FWD_8K, DECODE_16K
+
+    # Inputs drawn on the GPU and resident in HBM before timing starts.
+    q, k, v, do = attention_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, dev, q_mult=w.q_mult,
+                                   with_dout=True)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_b = fa.bwd_workspace(q)
+    qd, kd, vd = attention_inputs(wd.B, wd.H, 1, wd.d, wd.dtype, wd.seed, dev, Nkv=wd.Nkv)
+    od = torch.empty((wd.B, wd.H, 1, wd.d), dtype=wd.dtype, device=dev)
+    lsed = torch.empty((wd.B, wd.H), dtype=torch.float32, device=dev)
+    ws_d = fa.decode_workspace(kd, wd.splits)
+    torch.cuda.synchronize()
+
+    def step(ev):
+        ev[0].record()
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+        ev[1].record()
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws_b, w.scale, w.causal)
+        ev[2].record()
+        fa.fa_decode(qd, kd, vd, od, lsed, wd.scale, wd.splits, ws_d)
+        ev[3].record()
+
+    for _ in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+    ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps
+          for j, name in enumerate(("fwd", "bwd", "decode"))}
+
+    nn = w.B * w.H * w.N * w.N * w.d
+    fwd_flops = 4 * nn / 2
+    bwd_flops = 10 * nn / 2
+    elem = 2  # bf16 bytes
+    dec_bytes = (2 * wd.B * wd.H * wd.Nkv * wd.d + 2 * wd.B * wd.H * wd.d) * elem
+    fwd_tf = fwd_flops / (ms["fwd"] * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (ms["bwd"] * 1e-3) / 1e12
+    dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9
+    value = (fwd_flops + bwd_flops) / ((ms["fwd"] + ms["bwd"]) * 1e-3) / 1e12
+
+    def roof(entry, bound, achieved, peak, unit):
+        return {"entry": entry, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(entry), "ms": round(ms[entry], 4)}
+
+    roofs = [roof("fwd", "mfma", fwd_tf, PEAK_BF16_TFLOPS, "TFLOP/s"),
+             roof("bwd", "mfma", bwd_tf, PEAK_BF16_TFLOPS, "TFLOP/s"),
+             roof("decode", "hbm", dec_gbs, PEAK_HBM_GBS, "GB/s")]
+    dominant = max(roofs, key=lambda r: r["ms"])
+
+    out = {
+        "metric": "fwd/bwd attention TFLOP/s (% MFMA peak) N=8192 d=128 bf16; decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attention fwd+bwd B1 H32 N8192 d128 bf16 causal (Q x2) + "
+                               "decode B64 H32 Nkv16384 d128 bf16 16 splits",
+                   "global_batch": w.B, "seq_len": w.N, "heads": w.H, "head_dim": w.d,
+                   "decode_batch": wd.B, "decode_kv_len": wd.Nkv, "decode_splits": wd.splits},
+        "fwd_tflops": round(fwd_tf, 2),
+        "bwd_tflops": round(bwd_tf, 2),
+        "decode_gbs": round(dec_gbs, 2),
+        "roofline": dominant,
+        "rooflines": roofs,
+        "wall_s_timed": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(q, k, v, do, lse, None, args.cpu_heads, w.scale)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * fa.h -- C ABI of libfa: exact, IO-aware scaled-dot-product attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes O = softmax(scale * Q K^T [+ causal mask]) V without
+ * ever writing the N x N score or probability matrix to device memory: for
+ * each block of query rows, key/value tiles stream through on-chip memory
+ * and a running maximum and running sum rescale the partial output ("FlashAttention
+ * ontleed", § "Algoritmische kern in pseudocode"; Lensa ML explainer, Steps 3
+ * and 4).  Three calls make up the library:
+ *
+ *   fa_fwd     fused forward; writes O and the per-row log-sum-exp L.
+ *   fa_bwd     backward by recomputation from Q, K, V, O and L ("03.
+ *              FlashAttention", § "Backward pass"); writes dQ, dK, dV.
+ *   fa_decode  one query token per head against a long key/value history,
+ *              split across workgroups and merged by log-sum-exp ("FlashAttention
+ *              ontleed", § "Interactie met de KV-cache tijdens inferentie";
+ *              "03. FlashAttention", § "Variantes et extensions").
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense, row-major [B, H, N, d] (d contiguous, then N, H, B),
+ *     in device memory, of element type `dt` (IEEE fp16 or bfloat16).
+ *   - d (head dimension) must be 64 or 128.
+ *   - L ("lse") is float32 [B, H, N]: the natural-log log-sum-exp of row i's
+ *     scaled, masked scores, L_i = m_i + ln(l_i) in the pages' notation
+ *     (running max m and running sum l).
+ *   - causal != 0: key j is visible to query i iff j <= i (query and key
+ *     positions both count from 0; N_q = N_k in fa_fwd and fa_bwd).
+ *   - scale must be finite and > 0 (the pages use 1/sqrt(d)).
+ *   - Arithmetic: fp16/bf16 MFMA products with fp32 accumulation; softmax
+ *     statistics in fp32; P is rounded to `dt` before the P V product;
+ *     outputs are rounded to nearest even.
+ *   - Pointers to fp16/bf16 tensors and workspaces must be 16-byte aligned;
+ *     float32 pointers 4-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work and return; errors during execution surface at the
+ *     caller's next synchronisation.
+ *   - Ownership: the caller allocates and owns every buffer, including the
+ *     workspaces sized by the *_workspace_bytes queries.  The library never
+ *     allocates or frees device memory and keeps no state between calls.
+ *     Outputs must not alias inputs.
+ *   - Errors: every argument is validated before any HIP call; on error
+ *     nothing is enqueued and no output is touched.  No C++ exception
+ *     crosses this interface.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* B, H, N, Nkv < 1, sizes overflow, or bad scale */
+  FA_ERR_DTYPE = 3,       /* dt is not FA_F16 or FA_BF16 */
+  FA_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+  FA_ERR_UNSUPPORTED = 5, /* head dimension other than 64 or 128 */
+  FA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the query says */
+  FA_ERR_HIP = 7,         /* the HIP runtime refused a launch */
+  FA_ERR_SPLITS = 8       /* num_splits < 1 or above FA_MAX_SPLITS */
+} fa_status;
+
+typedef enum fa_dtype { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+#define FA_MAX_SPLITS 256
+
+/*
+ * Fused forward ("FlashAttention ontleed", § "Algoritmische kern in
+ * pseudocode"; "03. FlashAttention", § "Mécanisme").
+ *   q, k, v  in : [B, H, N, d], dt
+ *   o        out: [B, H, N, d], dt      -- softmax(scale * q k^T [masked]) v
+ *   lse      out: [B, H, N], float32    -- per-row natural-log log-sum-exp
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, fa_dtype dt,
+                 void* stream);
+
+/* Bytes of device workspace fa_bwd needs: a float32 dQ accumulator
+ * [B, H, N, d] and the float32 row terms D [B, H, N], 256-byte aligned. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward by recomputation ("FlashAttention ontleed", § "Geheugencomplexiteit:
+ * van O(N²) naar O(N)"; "03. FlashAttention", § "Backward pass"): P is rebuilt
+ * on chip from q, k and the saved lse instead of being stored.
+ *   q, k, v, o, dout in : [B, H, N, d], dt (o and lse exactly as fa_fwd wrote
+ *                         them for the same q, k, v, scale, causal)
+ *   lse             in : [B, H, N], float32
+ *   dq, dk, dv      out: [B, H, N, d], dt
+ *   workspace           : device scratch of at least fa_bwd_workspace_bytes;
+ *                         contents on entry are ignored, on exit undefined.
+ * dq is accumulated with float32 atomics, so its low bits may differ between
+ * runs; dk and dv are deterministic.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                 float scale, int causal, fa_dtype dt, void* stream);
+
+/* Bytes of device workspace fa_decode needs: per-split float32 partial
+ * outputs [B, H, num_splits, d] and log-sum-exps [B, H, num_splits]. */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
+ * Split-history decode for one query token per head ("FlashAttention ontleed",
+ * § "Interactie met de KV-cache tijdens inferentie"; Lensa ML explainer,
+ * question on decoding).  The Nkv keys of each head are cut into num_splits
+ * contiguous chunks of ceil(Nkv / num_splits) keys (the last may be shorter
+ * or empty); each chunk yields its normalised partial output and its
+ * log-sum-exp, and a second kernel merges the chunks by the online-softmax
+ * rescaling rule (Lensa ML explainer, Step 4).  No mask.
+ *   q        in : [B, H, 1, d], dt
+ *   k, v     in : [B, H, Nkv, d], dt
+ *   o        out: [B, H, 1, d], dt
+ *   lse      out: [B, H] float32, or NULL if not wanted
+ *   workspace   : device scratch of at least fa_decode_workspace_bytes.
+ */
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Nkv, int d, float scale, int num_splits,
+                    void* workspace, size_t workspace_bytes, fa_dtype dt, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_string(fa_status s);
+
+/* Library version as "major.minor.patch" (static string). */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,135 @@
+"""The C ABI of libfa: exports and argument validation (CPU only).
+
+libfa validates every argument before any HIP call, so every error path is
+reachable without a GPU.  Fake (but suitably aligned) device addresses are
+passed where a pointer must merely be non-NULL; validation never
+dereferences them and these calls fail before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_31_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+P = ctypes.c_void_p(0x10000)        # aligned stand-in pointer, never dereferenced
+P_ODD = ctypes.c_void_p(0x10002)    # 2-byte aligned only
+NULL = ctypes.c_void_p(0)
+ERR = {v: k for k, v in fa.STATUS_NAMES.items()}
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_decode", "fa_bwd_workspace_bytes",
+                          "fa_decode_workspace_bytes", "fa_status_string", "fa_version"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/fa.h but not exported"
+
+
+def test_status_strings_and_version(lib):
+    for code, name in fa.STATUS_NAMES.items():
+        assert fa.fa_status_string(code).startswith(name)
+    assert "unknown" in fa.fa_status_string(99)
+    assert re.fullmatch(r"\d+\.\d+\.\d+", fa.fa_version())
+
+
+def test_workspace_sizes(lib):
+    # fp32 dQ accumulator + fp32 row terms, each rounded up to 256 bytes
+    assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 128 * 4 + 2 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 768 + 256
+    # fp32 partial outputs + fp32 partial lse
+    assert fa.fa_decode_workspace_bytes(64, 32, 128, 16) == 64 * 32 * 16 * 128 * 4 + 64 * 32 * 16 * 4
+    assert fa.fa_decode_workspace_bytes(1, 1, 64, 3) == 768 + 256
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+    assert fa.fa_decode_workspace_bytes(1, 1, 64, 0) == 0
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, scale=0.125, causal=0, dt=1):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dt, NULL)
+
+
+def test_fwd_validation(lib):
+    for kw in ("q", "k", "v", "o", "lse"):
+        assert fwd(lib, **{kw: NULL}) == ERR["FA_ERR_NULL"]
+    assert fwd(lib, dt=2) == ERR["FA_ERR_DTYPE"]
+    for kw in ("B", "H", "N"):
+        assert fwd(lib, **{kw: 0}) == ERR["FA_ERR_SHAPE"]
+        assert fwd(lib, **{kw: -3}) == ERR["FA_ERR_SHAPE"]
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert fwd(lib, scale=bad) == ERR["FA_ERR_SHAPE"]
+    for d in (32, 96, 256, 0):
+        assert fwd(lib, d=d) == ERR["FA_ERR_UNSUPPORTED"]
+    assert fwd(lib, B=1 << 20, H=1 << 10, N=1 << 20) == ERR["FA_ERR_SHAPE"]
+    for kw in ("q", "k", "v", "o"):
+        assert fwd(lib, **{kw: P_ODD}) == ERR["FA_ERR_ALIGN"]
+    assert fwd(lib, lse=P_ODD) == ERR["FA_ERR_ALIGN"]
+
+
+def bwd(lib, ws=P, ws_bytes=1 << 30, B=1, H=1, N=16, d=64, dt=0, scale=0.125, **ptrs):
+    p = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P)
+    p.update(ptrs)
+    return lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"],
+                      p["dv"], ws, ws_bytes, B, H, N, d, scale, 1, dt, NULL)
+
+
+def test_bwd_validation(lib):
+    for kw in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv"):
+        assert bwd(lib, **{kw: NULL}) == ERR["FA_ERR_NULL"]
+    assert bwd(lib, dt=7) == ERR["FA_ERR_DTYPE"]
+    assert bwd(lib, N=0) == ERR["FA_ERR_SHAPE"]
+    assert bwd(lib, d=80) == ERR["FA_ERR_UNSUPPORTED"]
+    assert bwd(lib, ws=NULL) == ERR["FA_ERR_WORKSPACE"]
+    need = fa.fa_bwd_workspace_bytes(1, 1, 16, 64)
+    assert bwd(lib, ws_bytes=need - 1) == ERR["FA_ERR_WORKSPACE"]
+    for kw in ("q", "dout", "dq", "dk", "dv"):
+        assert bwd(lib, **{kw: P_ODD}) == ERR["FA_ERR_ALIGN"]
+    assert bwd(lib, ws=P_ODD) == ERR["FA_ERR_ALIGN"]
+
+
+def dec(lib, q=P, k=P, v=P, o=P, lse=P, B=2, H=3, Nkv=100, d=128, scale=0.1, splits=4, ws=P,
+        ws_bytes=1 << 30, dt=1):
+    return lib.fa_decode(q, k, v, o, lse, B, H, Nkv, d, scale, splits, ws, ws_bytes, dt, NULL)
+
+
+def test_decode_validation(lib):
+    for kw in ("q", "k", "v", "o"):
+        assert dec(lib, **{kw: NULL}) == ERR["FA_ERR_NULL"]
+    assert dec(lib, Nkv=0) == ERR["FA_ERR_SHAPE"]
+    assert dec(lib, d=48) == ERR["FA_ERR_UNSUPPORTED"]
+    assert dec(lib, dt=-1) == ERR["FA_ERR_DTYPE"]
+    assert dec(lib, splits=0) == ERR["FA_ERR_SPLITS"]
+    assert dec(lib, splits=fa.FA_MAX_SPLITS + 1) == ERR["FA_ERR_SPLITS"]
+    assert dec(lib, ws=NULL) == ERR["FA_ERR_WORKSPACE"]
+    need = fa.fa_decode_workspace_bytes(2, 3, 128, 4)
+    assert dec(lib, ws_bytes=need - 4) == ERR["FA_ERR_WORKSPACE"]
+    assert dec(lib, k=P_ODD) == ERR["FA_ERR_ALIGN"]
+    assert dec(lib, lse=P_ODD) == ERR["FA_ERR_ALIGN"]
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attention_fwd(q, q, q)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q.float(), q, q, q, torch.zeros(1, 1, 16), 0.1, False)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        fa.load_library(str(tmp_path / "libfa.so"))
