@@ -13,6 +13,11 @@ HIP events recorded on the stream its kernels run on (torch's current
 stream, which the binding hands to the library).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--only fwd|bwd|decode]
+--only runs a single entry point per step (for per-kernel profiling); the
+JSON line then carries only that entry's figures.
+--copy-calibration BYTES only copies a BYTES-sized device buffer 5 times
+(a plain copy kernel of known traffic, used to scale HBM byte counters).
 """
 import argparse
 import hashlib
@@ -71,6 +76,25 @@ def cpu_baseline(q, k, v, do, lse_unused, decode_inputs, heads: int, scale: floa
                       f"N={n} d={d} causal workload ({secs:.1f} s; useful-FLOP formula)"}
 
 
+def copy_calibration(torch, nbytes: int, reps: int = 5):
+    """Time a plain device-to-device copy of nbytes (reads nbytes, writes nbytes)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": src.numel() * 4,
+                      "reps": reps, "ms_per_copy": round(ms, 4),
+                      "gbs_read_plus_write": round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,6 +102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--only", choices=("fwd", "bwd", "decode"), default=None)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this attention path runs on a single GPU "
@@ -86,6 +112,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
 
     import exact_io_aware_31_amd as fa
     from synth_inputs import DECODE_16K, FWD_8K, attention_inputs
@@ -108,13 +138,20 @@ def main():
     ws_d = fa.decode_workspace(kd, wd.splits)
     torch.cuda.synchronize()
 
+    run = {e: args.only in (None, e) for e in ("fwd", "bwd", "decode")}
+    if run["bwd"] and not run["fwd"]:  # the backward consumes a forward's O and lse
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+
     def step(ev):
         ev[0].record()
-        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+        if run["fwd"]:
+            fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
         ev[1].record()
-        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws_b, w.scale, w.causal)
+        if run["bwd"]:
+            fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws_b, w.scale, w.causal)
         ev[2].record()
-        fa.fa_decode(qd, kd, vd, od, lsed, wd.scale, wd.splits, ws_d)
+        if run["decode"]:
+            fa.fa_decode(qd, kd, vd, od, lsed, wd.scale, wd.splits, ws_d)
         ev[3].record()
 
     for _ in range(args.warmup):
@@ -140,10 +177,16 @@ def main():
     bwd_flops = 10 * nn / 2
     elem = 2  # bf16 bytes
     dec_bytes = (2 * wd.B * wd.H * wd.Nkv * wd.d + 2 * wd.B * wd.H * wd.d) * elem
-    fwd_tf = fwd_flops / (ms["fwd"] * 1e-3) / 1e12
-    bwd_tf = bwd_flops / (ms["bwd"] * 1e-3) / 1e12
-    dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9
-    value = (fwd_flops + bwd_flops) / ((ms["fwd"] + ms["bwd"]) * 1e-3) / 1e12
+    def rate(amount, entry):
+        return amount / (ms[entry] * 1e-3) if run[entry] and ms[entry] > 0 else 0.0
+
+    fwd_tf = rate(fwd_flops, "fwd") / 1e12
+    bwd_tf = rate(bwd_flops, "bwd") / 1e12
+    dec_gbs = rate(dec_bytes, "decode") / 1e9
+    if args.only is None:
+        value = (fwd_flops + bwd_flops) / ((ms["fwd"] + ms["bwd"]) * 1e-3) / 1e12
+    else:
+        value = {"fwd": fwd_tf, "bwd": bwd_tf, "decode": dec_gbs}[args.only]
 
     def roof(entry, bound, achieved, peak, unit):
         return {"entry": entry, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
@@ -153,12 +196,13 @@ def main():
     roofs = [roof("fwd", "mfma", fwd_tf, PEAK_BF16_TFLOPS, "TFLOP/s"),
              roof("bwd", "mfma", bwd_tf, PEAK_BF16_TFLOPS, "TFLOP/s"),
              roof("decode", "hbm", dec_gbs, PEAK_HBM_GBS, "GB/s")]
+    roofs = [r for r in roofs if run[r["entry"]]]
     dominant = max(roofs, key=lambda r: r["ms"])
 
     out = {
         "metric": "fwd/bwd attention TFLOP/s (% MFMA peak) N=8192 d=128 bf16; decode HBM GB/s",
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": "GB/s" if args.only == "decode" else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -179,7 +223,9 @@ def main():
         "rooflines": roofs,
         "wall_s_timed": round(t_wall, 3),
     }
-    if not args.no_cpu_baseline:
+    if args.only is not None:
+        out["only"] = args.only
+    if not args.no_cpu_baseline and args.only is None:
         out["cpu_baseline"] = cpu_baseline(q, k, v, do, lse, None, args.cpu_heads, w.scale)
     print(json.dumps(out), flush=True)
 

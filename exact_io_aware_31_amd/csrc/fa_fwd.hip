@@ -10,52 +10,74 @@
 // lse = m + ln(l).
 //
 // MI355X mapping (not the pages' A100 tile rule):
-//   * 4 waves x 32 query rows = 128 rows per workgroup, 64-key tiles.
+//   * NW waves x (32 * QG) query rows per workgroup, two waves per SIMD;
+//     64-key tiles.
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
-//     each lane then owns ONE query row (column l % 32) and 16 of its scores
-//     per 32-key block, so the row max / row sum are in-lane reductions plus
-//     one v_permlane32_swap between the two wave halves.
+//     each lane then owns ONE query row per 32-row group (column l % 32) and
+//     16 of its scores per 32-key block, so the row max / row sum are in-lane
+//     reductions plus one v_permlane32_swap between the two wave halves.
 //   * The probabilities stay in registers and feed O^T += V^T P^T directly
 //     as the B operand: the accumulator layout of S^T is used as the operand
-//     layout with a consistent permutation of the reduction index, and the
-//     V tile is stored transposed in LDS in that same key order.
-//   * exp2 with log2(e) folded into the scale (v_exp_f32).
-//   * Causal: tiles entirely above the diagonal are never loaded; per wave,
-//     tiles entirely above its 32 rows are skipped; only tiles that cross the
-//     diagonal (or the ragged end) are masked element-wise.
+//     layout with a consistent permutation of the reduction index.  The A
+//     operand V^T is read from the row-major V tile with the LDS transpose
+//     read (ds_read_b64_tr_b16), so V is never transposed in memory.
+//   * K and V tiles are double-buffered in LDS; the next tile's global loads
+//     are issued before the current tile is computed, so their latency hides
+//     behind the matrix work; one barrier per tile.
+//   * Running max in log2 units with log2(e) folded into the scale (v_exp_f32).
+//     The output is rescaled only when a row's maximum grows by more than
+//     2^8: until then the stale maximum is kept as the reference, which leaves
+//     O / l and lse exact (both use the same reference) and keeps every
+//     exponentiated score below 2^8.
+//   * Causal: tiles entirely above the diagonal are never loaded; per
+//     32-row group, tiles entirely above its rows are skipped; only tiles that
+//     cross the diagonal (or the ragged end) are masked element-wise.
 //   * Grid: consecutive work items of one head are placed on one XCD (the
 //     hardware deals workgroups round-robin over the 8 XCDs) so the head's
 //     K/V stay in that XCD's L2; causal query blocks run heaviest first.
 #include "fa_common.h"
 #include "fa_launch.h"
 
+#ifndef FA_FWD_NW
+#define FA_FWD_NW 8
+#endif
+#ifndef FA_FWD_QG
+#define FA_FWD_QG 1
+#endif
+
 namespace fa {
 
-constexpr int FWD_BR = 128;
+constexpr int FWD_NW = FA_FWD_NW;  // waves per workgroup
+constexpr int FWD_QG = FA_FWD_QG;  // 32-row query groups per wave
+constexpr int FWD_BR = FWD_NW * 32 * FWD_QG;
 constexpr int FWD_BC = 64;
-constexpr int FWD_THREADS = 256;
+constexpr float FWD_RESCALE_SLACK = 8.0f;  // log2 units
 
-// Position of key k (0 <= k < FWD_BC) inside a transposed V tile row.  Within
-// each group of 16 keys the four quads are stored in the order 0, 2, 1, 3,
-// which is the order in which the S^T accumulator hands probabilities to the
-// two wave halves (see fa_common.h).
-__device__ __forceinline__ int vt_pos_of_quad(int kq) {
-  const int quad = kq & 3;
-  const int perm = (quad == 1) ? 2 : (quad == 2) ? 1 : quad;
-  return (kq >> 2) * 16 + perm * 4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i mod 4) of the 4-element rows addressed by lanes i/4, 4 + i/4, 8 + i/4
+// and 12 + i/4 of its group.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
 }
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
+template <typename T, int D, bool CAUSAL, int NW, int QG>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, float c) {
   using v8 = typename Vec<T>::v8;
   using v4 = typename Vec<T>::v4;
-  constexpr int BR = FWD_BR, BC = FWD_BC;
-  constexpr int KSTR = D + 8;   // K tile row stride (elements); +16 B against bank conflicts
-  constexpr int VSTR = BC + 8;  // V^T tile row stride (elements)
-  __shared__ __attribute__((aligned(16))) T Ks[BC * KSTR];
-  __shared__ __attribute__((aligned(16))) T Vt[D * VSTR];
+  constexpr int NT = NW * 64;
+  constexpr int BR = NW * 32 * QG, BC = FWD_BC;
+  constexpr int KSTR = D + 8;   // K rows: 16-byte pad, conflict-free 16-byte row reads
+  constexpr int VSTR = D + 16;  // V rows: 32-byte pad, conflict-free transpose reads
+  constexpr int CH = BC * D / 8;                 // 16-byte chunks per tile
+  constexpr int CPT = (CH + NT - 1) / NT;        // chunks per thread
+  __shared__ __attribute__((aligned(16))) T Ks[2][BC * KSTR];
+  __shared__ __attribute__((aligned(16))) T Vs[2][BC * VSTR];
 
   // Work item: XCD-local heads, heaviest causal query blocks first.
   const int p = blockIdx.x;
@@ -70,137 +92,206 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_kernel(
   const T* __restrict__ Kh = K + hoff;
   const T* __restrict__ Vh = V + hoff;
 
-  const int q0 = qb * BR + wave * 32;  // first query row of this wave
-  const int myq = q0 + l32;            // the query row this lane owns
+  const int qw0 = qb * BR + wave * 32 * QG;  // first query row of this wave
+  int myq[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) myq[g] = qw0 + 32 * g + l32;
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[myq][16 kk + 8 hh + 0..7].
-  v8 qf[D / 16];
+  v8 qf[QG][D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (myq < N) qf[kk] = ld16<v8>(Qh + (size_t)myq * D + 16 * kk + 8 * hh);
-    else qf[kk] = v8{};
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[g][kk] = (myq[g] < N) ? ld16<v8>(Qh + (size_t)myq[g] * D + 16 * kk + 8 * hh) : v8{};
+
+  f32x16 oacc[QG][D / 32];
+  float m_run[QG], l_run[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[g][i] = f32x16{};
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
   }
 
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // running max of scaled scores, log2 units
-  float l_run = 0.f;        // running sum over this wave half's keys
-
-  const int kv_end = CAUSAL ? min(N, qb * BR + BR) : N;
+  const int kv_end = CAUSAL ? min(N, (qb + 1) * BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
 
+  // Tile staging: thread moves chunks tid, tid + NT, ... of the K and V tiles.
+  // Rows past the end are clamped to row N-1: those keys are masked to -inf
+  // before the softmax, so their probabilities (and their V rows' weight) are 0.
+  u32x4 kpre[CPT], vpre[CPT];
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int e = tid + i * NT;
+      if (CH % NT == 0 || e < CH) {
+        const int row = min(kb + e / (D / 8), N - 1), c8 = e % (D / 8);
+        const size_t off = (size_t)row * D + 8 * c8;
+        kpre[i] = *reinterpret_cast<const u32x4*>(Kh + off);
+        vpre[i] = *reinterpret_cast<const u32x4*>(Vh + off);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int e = tid + i * NT;
+      if (CH % NT == 0 || e < CH) {
+        const int row = e / (D / 8), c8 = e % (D / 8);
+        *reinterpret_cast<u32x4*>(&Ks[buf][row * KSTR + 8 * c8]) = kpre[i];
+        *reinterpret_cast<u32x4*>(&Vs[buf][row * VSTR + 8 * c8]) = vpre[i];
+      }
+    }
+  };
+
+  // Per-lane offsets of the transpose reads that build the V^T operand:
+  // lane i of 16-lane group G addresses key 4 hh + i / 4 (+ 8 t), columns
+  // 16 (G mod 2) + 4 (i mod 4) (+ 32 nb).
+  const int grp = lane >> 4, li = lane & 15;
+  const int voff = (4 * hh + (li >> 2)) * VSTR + 16 * (grp & 1) + 4 * (li & 3);
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
   for (int j = 0; j < ntiles; ++j) {
-    const int kb = j * BC;
-    __syncthreads();  // every wave is done reading the previous tile
-    // K tile, row-major, 16-byte chunks (a wave covers 4 rows contiguously).
-    constexpr int KCH = BC * D / 8;
-#pragma unroll
-    for (int e = tid; e < KCH; e += FWD_THREADS) {
-      const int row = e / (D / 8), c8 = e % (D / 8);
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (kb + row < N) val = *reinterpret_cast<const u32x4*>(Kh + (size_t)(kb + row) * D + 8 * c8);
-      *reinterpret_cast<u32x4*>(&Ks[row * KSTR + 8 * c8]) = val;
-    }
-    // V tile, transposed: a thread moves 4 keys x 8 columns.
-    constexpr int VUNITS = (BC / 4) * (D / 8);
-#pragma unroll
-    for (int u = tid; u < VUNITS; u += FWD_THREADS) {
-      const int c8 = u % (D / 8), kq = u / (D / 8);
-      v8 rows[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + 4 * kq + i;
-        rows[i] = (key < N) ? ld16<v8>(Vh + (size_t)key * D + 8 * c8) : v8{};
-      }
-      const int pos = vt_pos_of_quad(kq);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v4 col = {rows[0][e], rows[1][e], rows[2][e], rows[3][e]};
-        *reinterpret_cast<u32x2*>(&Vt[(8 * c8 + e) * VSTR + pos]) = __builtin_bit_cast(u32x2, col);
-      }
-    }
-    __syncthreads();
-    if (CAUSAL && kb > q0 + 31) continue;  // whole tile above this wave's rows
+    const int kb = j * BC, buf = j & 1;
+    if (j + 1 < ntiles) load_tile(kb + BC);  // in flight while tile j is computed
 
-    // S^T = K Q^T for BC/32 blocks of 32 keys.
-    f32x16 sacc[BC / 32];
+    bool active[QG];
+    bool any_active = false;
 #pragma unroll
-    for (int sb = 0; sb < BC / 32; ++sb) {
-      sacc[sb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const v8 a = *reinterpret_cast<const v8*>(&Ks[(32 * sb + l32) * KSTR + 16 * kk + 8 * hh]);
-        sacc[sb] = mfma32x32x16(a, qf[kk], sacc[sb]);
-      }
+    for (int g = 0; g < QG; ++g) {
+      active[g] = !CAUSAL || kb <= qw0 + 32 * g + 31;
+      any_active |= active[g];
     }
-
-    // Mask keys past the end and, on diagonal tiles, keys after the query.
-    const bool need_mask = (CAUSAL && kb + BC - 1 > q0) || (kb + BC > N);
-    if (need_mask) {
+    if (any_active) {
+      const T* __restrict__ kt = Ks[buf];
+      const T* __restrict__ vt = Vs[buf];
+      // S^T = K Q^T for BC/32 blocks of 32 keys; the blocks are interleaved so
+      // consecutive MFMAs are independent, and each K operand is read from LDS
+      // one step before the MFMA that uses it.
+      f32x16 sacc[QG][BC / 32];
+#pragma unroll
+      for (int g = 0; g < QG; ++g)
+#pragma unroll
+        for (int sb = 0; sb < BC / 32; ++sb) sacc[g][sb] = f32x16{};
+      const T* krow = kt + l32 * KSTR + 8 * hh;
+      v8 ka[2][BC / 32];
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb)
+        ka[0][sb] = *reinterpret_cast<const v8*>(krow + 32 * sb * KSTR);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= N || (CAUSAL && key > myq)) sacc[sb][r] = -INFINITY;
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk + 1 < D / 16) {
+#pragma unroll
+          for (int sb = 0; sb < BC / 32; ++sb)
+            ka[(kk + 1) & 1][sb] = *reinterpret_cast<const v8*>(krow + 32 * sb * KSTR + 16 * (kk + 1));
+        }
+#pragma unroll
+        for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+          for (int g = 0; g < QG; ++g)
+            if (active[g]) sacc[g][sb] = mfma32x32x16(ka[kk & 1][sb], qf[g][kk], sacc[g][sb]);
+      }
+
+      v8 pb[QG][BC / 16];
+#pragma unroll
+      for (int g = 0; g < QG; ++g) {
+        if (!active[g]) {
+#pragma unroll
+          for (int kc = 0; kc < BC / 16; ++kc) pb[g][kc] = v8{};
+          continue;
+        }
+        // Mask keys past the end and, on diagonal tiles, keys after the query:
+        // key kb + 32 sb + 8 (r / 4) + 4 hh + (r % 4) is kept iff its offset
+        // within the tile is <= lim (a per-lane bound, so 2 VALU ops per score).
+        const bool need_mask = (CAUSAL && kb + BC - 1 > qw0 + 32 * g) || (kb + BC > N);
+        if (need_mask) {
+          int lim = N - 1 - kb;
+          if (CAUSAL) lim = min(lim, myq[g] - kb);
+          lim -= 4 * hh;
+#pragma unroll
+          for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * sb + 8 * (r >> 2) + (r & 3) > lim) sacc[g][sb][r] = -INFINITY;
+        }
+        // Tile row max (3-input max tree), shared by the two halves of the wave.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 4)
+            mx = fmaxf(fmaxf(mx, sacc[g][sb][r]),
+                       fmaxf(fmaxf(sacc[g][sb][r + 1], sacc[g][sb][r + 2]), sacc[g][sb][r + 3]));
+        mx = fmaxf(mx, other_half(mx));
+        const float m_cand = mx * c;
+        if (__ballot(m_cand > m_run[g] + FWD_RESCALE_SLACK)) {
+          const float m_new = fmaxf(m_run[g], m_cand);
+          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[g] - m_new);
+          l_run[g] *= alpha;
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) oacc[g][nb] *= alpha;
+          m_run[g] = m_new;
+        }
+        const float mref = m_run[g];
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial row sums
+#pragma unroll
+        for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              pv[e] = fast_exp2(__builtin_fmaf(sacc[g][sb][8 * hf + e], c, -mref));
+              rs[e & 3] += pv[e];
+            }
+            pb[g][2 * sb + hf] = to_v8<T>(pv);
+          }
+        l_run[g] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      }
+
+      // O^T += V^T P^T; the V^T operand comes from two transpose reads.
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int kc = 0; kc < BC / 16; ++kc) {
+          const T* vp = vt + voff + (16 * kc) * VSTR + 32 * nb;
+          const u32x2 lo = lds_read_tr16(vp);
+          const u32x2 hi = lds_read_tr16(vp + 8 * VSTR);
+          const u32x4 cat = {lo[0], lo[1], hi[0], hi[1]};
+          const v8 a = __builtin_bit_cast(v8, cat);
+#pragma unroll
+          for (int g = 0; g < QG; ++g)
+            if (active[g]) oacc[g][nb] = mfma32x32x16(a, pb[g][kc], oacc[g][nb]);
         }
     }
 
-    // Online softmax update for this lane's query row.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sb = 0; sb < BC / 32; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-    mx = fmaxf(mx, other_half(mx));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = fast_exp2(m_run - m_new);
-    float rs = 0.f;
-    v8 pb[BC / 16];
-#pragma unroll
-    for (int sb = 0; sb < BC / 32; ++sb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = fast_exp2(__builtin_fmaf(sacc[sb][8 * hf + e], c, -m_new));
-          rs += pe;
-          pv[e] = pe;
-        }
-        pb[2 * sb + hf] = to_v8<T>(pv);
-      }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) oacc[nb] *= alpha;
-
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-      for (int kc = 0; kc < BC / 16; ++kc) {
-        const v8 a = *reinterpret_cast<const v8*>(&Vt[(32 * nb + l32) * VSTR + 16 * kc + 8 * hh]);
-        oacc[nb] = mfma32x32x16(a, pb[kc], oacc[nb]);
-      }
-    m_run = m_new;
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   // Epilogue: O = O / l, lse = (m + log2 l) ln 2.
-  const float l_tot = l_run + other_half(l_run);
-  const float inv = 1.f / l_tot;
-  if (myq < N) {
-    T* __restrict__ orow = O + hoff + (size_t)myq * D;
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb)
+  for (int g = 0; g < QG; ++g) {
+    const float l_tot = l_run[g] + other_half(l_run[g]);
+    const float inv = 1.f / l_tot;
+    if (myq[g] < N) {
+      T* __restrict__ orow = O + hoff + (size_t)myq[g] * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        v4 vals;
+      for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) vals[q] = (T)(oacc[nb][4 * g + q] * inv);
-        *reinterpret_cast<u32x2*>(orow + 32 * nb + 8 * g + 4 * hh) = __builtin_bit_cast(u32x2, vals);
-      }
-    if (hh == 0) LSE[(size_t)bh * N + myq] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+        for (int gg = 0; gg < 4; ++gg) {
+          v4 vals;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) vals[q] = (T)(oacc[g][nb][4 * gg + q] * inv);
+          *reinterpret_cast<u32x2*>(orow + 32 * nb + 8 * gg + 4 * hh) = __builtin_bit_cast(u32x2, vals);
+        }
+      if (hh == 0) LSE[(size_t)bh * N + myq[g]] = (m_run[g] + log2f(l_tot)) * 0.69314718055994531f;
+    }
   }
 }
 
@@ -209,8 +300,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const int nqb = (a.N + FWD_BR - 1) / FWD_BR;
   const int total = a.B * a.H * nqb;
   const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(total), dim3(FWD_THREADS), 0, s,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, FWD_NW, FWD_QG>), dim3(total), dim3(FWD_NW * 64), 0,
+                     s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.N, nqb, total, c);
   return hipGetLastError();
 }

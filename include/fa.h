@@ -27,6 +27,8 @@
  *   - causal != 0: key j is visible to query i iff j <= i (query and key
  *     positions both count from 0; N_q = N_k in fa_fwd and fa_bwd).
  *   - scale must be finite and > 0 (the pages use 1/sqrt(d)).
+ *   - Input values must be finite; results for inputs holding NaN or Inf
+ *     are unspecified.
  *   - Arithmetic: fp16/bf16 MFMA products with fp32 accumulation; softmax
  *     statistics in fp32; P is rounded to `dt` before the P V product;
  *     outputs are rounded to nearest even.
