@@ -18,24 +18,45 @@
 //      it walks the query blocks (only blocks at or below the diagonal when
 //      causal).  Per 64-query block: S and dP with v_mfma_f32_32x32x16 (keys
 //      on the lanes), P and dS in registers, dV += P^T dO and dK += dS^T Q
-//      straight from those registers (the same reduction-index permutation as
-//      the forward), dS through LDS once so the four waves can form
-//      dQ = dS K for the whole 128-key block, added to fp32 dQ with atomics.
+//      straight from those registers (the B operands dO^T and Q^T come from
+//      the row-major tiles through the LDS transpose read), dS^T through LDS
+//      once so the four waves can form dQ = dS K for the whole 128-key block,
+//      added to the fp32 dQ accumulator with atomics.
 //   3. bwd_dq:   dQ = scale * accumulator, rounded to the storage type.
+//
+// Pipelining in bwd_main: the next query block's Q, dO, L and D are loaded
+// into registers while the current block is computed; tiles and the dS^T
+// block are double-buffered in LDS, and the dQ product of a block runs one
+// step later, so each step needs a single barrier.
+//
+// LDS layout: row-major tiles without padding, 16-byte chunk c of row r
+// stored at chunk c ^ sw(r), sw(r) = 2 (r mod 4) + (r / 4 mod 2).  Eight
+// consecutive rows then hit eight different chunks (16-byte row reads are
+// conflict-free) and four consecutive rows hit four different chunk pairs
+// (transpose reads are conflict-free).
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 
 constexpr int BWD_BK = 128;  // keys per workgroup (4 waves x 32)
-constexpr int BWD_BQ = 64;   // query rows per inner step
+constexpr int BWD_BQ = 64;   // query rows per step
 constexpr int BWD_THREADS = 256;
 
-// Same quad order as the forward's transposed V tile (see fa_fwd.hip).
-__device__ __forceinline__ int tr_pos_of_quad(int kq) {
-  const int quad = kq & 3;
-  const int perm = (quad == 1) ? 2 : (quad == 2) ? 1 : quad;
-  return (kq >> 2) * 16 + perm * 4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 bwd_read_tr16(const void* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Element offset of (row, col) in a swizzled row-major tile of ROWLEN elements.
+template <int ROWLEN>
+__device__ __forceinline__ int sw_off(int row, int col) {
+  return row * ROWLEN + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
 }
 
 // ---------------------------------------------------------------- kernel 1
@@ -70,25 +91,29 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ drow,
     float* __restrict__ dq_acc, T* __restrict__ dK, T* __restrict__ dV, int N, int nkb,
-    float scale, float c) {
+    int total, float scale, float c) {
   using v8 = typename Vec<T>::v8;
   using v4 = typename Vec<T>::v4;
   constexpr int BK = BWD_BK, BQ = BWD_BQ;
-  constexpr int RSTR = D + 8;    // row-major Q / dO tiles
-  constexpr int TSTR = BQ + 8;   // transposed Q / dO tiles
-  constexpr int SSTR = BK + 8;   // dS tile [query][key]
-  __shared__ __attribute__((aligned(16))) T Qs[BQ * RSTR];
-  __shared__ __attribute__((aligned(16))) T dOs[BQ * RSTR];
-  __shared__ __attribute__((aligned(16))) T QsT[D * TSTR];
-  __shared__ __attribute__((aligned(16))) T dOsT[D * TSTR];
-  __shared__ __attribute__((aligned(16))) T dSs[BQ * SSTR];
-  __shared__ float Ls2[BQ];
-  __shared__ float Dsh[BQ];
+  constexpr int NB = D / 32;          // 32-column blocks of D
+  constexpr int QB = BQ / 32;         // 32-row blocks of a query step
+  constexpr int CH = BQ * D / 8;      // 16-byte chunks per Q (or dO) tile
+  constexpr int CPT = CH / BWD_THREADS;
+  static_assert(CH % BWD_THREADS == 0, "tile chunks must divide evenly");
+  __shared__ __attribute__((aligned(16))) T Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) T dOs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) T dSt[2][BK * BQ];  // dS^T: [key][query]
+  __shared__ __attribute__((aligned(16))) float Ls2[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Dsh[2][BQ];
 
-  const int bh = blockIdx.x / nkb;
-  const int kblk = CAUSAL ? nkb - 1 - (blockIdx.x % nkb) : (blockIdx.x % nkb);
+  // Work item: XCD-local heads; causal key blocks heaviest (first) first.
+  const int p = blockIdx.x;
+  const int w = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
+  const int bh = w / nkb;
+  const int kblk = w % nkb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
+  const int li = lane & 15, grp = lane >> 4;
   const size_t hoff = (size_t)bh * N * D;
   const T* __restrict__ Qh = Q + hoff;
   const T* __restrict__ Kh = K + hoff;
@@ -109,112 +134,86 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
     kf[kk] = key_ok ? ld16<v8>(Kh + (size_t)mykey * D + 16 * kk + 8 * hh) : v8{};
     vf[kk] = key_ok ? ld16<v8>(Vh + (size_t)mykey * D + 16 * kk + 8 * hh) : v8{};
   }
-  // K as the B operand of dQ = dS K for this wave's column block(s) of dQ:
-  // lane holds K[kj0 + 16 ch + 8 hh + e][32 nb + l32], e = 0..7.
-  constexpr int NB = D / 32;          // column blocks of dQ
-  constexpr int QB = BQ / 32;         // row blocks of dQ
-  constexpr int PER_WAVE = NB * QB / 4;
+  // K as the B operand of dQ = dS K, in the key order the transpose read of
+  // dS^T produces: element e of lane half hh is key 8 (e / 4) + 4 hh + (e % 4)
+  // of each 16-key chunk; column 32 nb_q + l32.
+  constexpr int PER_WAVE = NB * QB / 4;  // dQ output blocks per wave
   const int nb_q = wave % NB;
   v8 ktf[BK / 16];
 #pragma unroll
-  for (int ch = 0; ch < BK / 16; ++ch) {
+  for (int ch = 0; ch < BK / 16; ++ch)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int key = kj0 + 16 * ch + 8 * hh + e;
+      const int key = kj0 + 16 * ch + 8 * (e >> 2) + 4 * hh + (e & 3);
       ktf[ch][e] = (key < N) ? Kh[(size_t)key * D + 32 * nb_q + l32] : (T)0.f;
     }
-  }
 
   f32x16 dvacc[NB], dkacc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) { dvacc[i] = f32x16{}; dkacc[i] = f32x16{}; }
 
-  const int qstart = CAUSAL ? kj0 : 0;
-  for (int qi0 = qstart; qi0 < N; qi0 += BQ) {
-    __syncthreads();  // previous step's readers of the shared tiles are done
-    // Stage Q_i and dO_i, row-major and transposed; L (log2 units) and D.
-    constexpr int UNITS = (BQ / 4) * (D / 8);
+  // Per-lane LDS offsets (elements).
+  //  * 16-byte row reads of Q / dO (A operands of S and dP): row 32 qb + l32,
+  //    chunk 2 kk + hh; the swizzle only changes the low 3 chunk bits, so the
+  //    offset is rowoff[kk mod 4] plus 8 chunks for kk >= 4.
+  int rowoff[4];
 #pragma unroll
-    for (int u = tid; u < UNITS; u += BWD_THREADS) {
-      const int c8 = u % (D / 8), kq = u / (D / 8);
-      v8 qr[4], dr[4];
+  for (int m = 0; m < 4; ++m) rowoff[m] = sw_off<D>(l32, 16 * m + 8 * hh);
+  //  * transpose reads of Q / dO (B operands of dK / dV): rows 16 kc + 8 t +
+  //    4 hh + li / 4, columns 32 nb + 16 (grp mod 2) + 4 (li mod 4).
+  const int trrow = 4 * hh + (li >> 2);
+  const int trcol = 16 * (grp & 1) + 4 * (li & 3);
+  //  * transpose reads of dS^T (A operand of dQ): rows (keys) 16 ch + 8 t +
+  //    4 hh + li / 4, columns (queries) 32 qb + 16 (grp mod 2) + 4 (li mod 4).
+  // Swizzle of a row depends only on row mod 8 = 8 t + trrow mod 8 = trrow + 8t.
+
+  u32x4 qpre[CPT], dpre[CPT];
+  float lpre = 0.f, dpre_row = 0.f;
+  auto load_step = [&](int qi0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qrow = qi0 + 4 * kq + i;
-        qr[i] = (qrow < N) ? ld16<v8>(Qh + (size_t)qrow * D + 8 * c8) : v8{};
-        dr[i] = (qrow < N) ? ld16<v8>(dOh + (size_t)qrow * D + 8 * c8) : v8{};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<v8*>(&Qs[(4 * kq + i) * RSTR + 8 * c8]) = qr[i];
-        *reinterpret_cast<v8*>(&dOs[(4 * kq + i) * RSTR + 8 * c8]) = dr[i];
-      }
-      const int pos = tr_pos_of_quad(kq);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v4 qc = {qr[0][e], qr[1][e], qr[2][e], qr[3][e]};
-        v4 dc = {dr[0][e], dr[1][e], dr[2][e], dr[3][e]};
-        *reinterpret_cast<u32x2*>(&QsT[(8 * c8 + e) * TSTR + pos]) = __builtin_bit_cast(u32x2, qc);
-        *reinterpret_cast<u32x2*>(&dOsT[(8 * c8 + e) * TSTR + pos]) = __builtin_bit_cast(u32x2, dc);
-      }
+    for (int i = 0; i < CPT; ++i) {
+      const int e = tid + i * BWD_THREADS;
+      const int row = min(qi0 + e / (D / 8), N - 1), c8 = e % (D / 8);
+      const size_t off = (size_t)row * D + 8 * c8;
+      qpre[i] = *reinterpret_cast<const u32x4*>(Qh + off);
+      dpre[i] = *reinterpret_cast<const u32x4*>(dOh + off);
     }
     if (tid < BQ) {
       const int qrow = qi0 + tid;
-      Ls2[tid] = (qrow < N) ? Lh[qrow] * 1.4426950408889634f : 0.f;
-      Dsh[tid] = (qrow < N) ? Dh[qrow] : 0.f;
+      lpre = (qrow < N) ? Lh[qrow] * 1.4426950408889634f : 0.f;
+      dpre_row = (qrow < N) ? Dh[qrow] : 0.f;
     }
-    __syncthreads();
-
-    // S = Q K_w^T and dP = dO V_w^T; P and dS stay in registers.
-    v8 pA[BQ / 16], dsA[BQ / 16];
+  };
+  auto store_step = [&](int buf) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const v8 aq = *reinterpret_cast<const v8*>(&Qs[(32 * qb + l32) * RSTR + 16 * kk + 8 * hh]);
-        s = mfma32x32x16(aq, kf[kk], s);
-        const v8 ad = *reinterpret_cast<const v8*>(&dOs[(32 * qb + l32) * RSTR + 16 * kk + 8 * hh]);
-        dp = mfma32x32x16(ad, vf[kk], dp);
-      }
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);  // query row in the block
-        const int qrow = qi0 + ql;
-        const bool ok = key_ok && qrow < N && (!CAUSAL || mykey <= qrow);
-        const float pe = ok ? fast_exp2(__builtin_fmaf(s[r], c, -Ls2[ql])) : 0.f;
-        pv[r] = pe;
-        dsv[r] = pe * (dp[r] - Dsh[ql]);
-        dSs[ql * SSTR + 32 * wave + l32] = (T)dsv[r];
-      }
-      pA[2 * qb] = to_v8<T>(pv);
-      pA[2 * qb + 1] = to_v8<T>(pv + 8);
-      dsA[2 * qb] = to_v8<T>(dsv);
-      dsA[2 * qb + 1] = to_v8<T>(dsv + 8);
+    for (int i = 0; i < CPT; ++i) {
+      const int e = tid + i * BWD_THREADS;
+      const int row = e / (D / 8), col = 8 * (e % (D / 8));
+      *reinterpret_cast<u32x4*>(&Qs[buf][sw_off<D>(row, col)]) = qpre[i];
+      *reinterpret_cast<u32x4*>(&dOs[buf][sw_off<D>(row, col)]) = dpre[i];
     }
+    if (tid < BQ) {
+      Ls2[buf][tid] = lpre;
+      Dsh[buf][tid] = dpre_row;
+    }
+  };
 
-    // dV_w += P^T dO_i and dK_w += dS^T Q_i (scale applied at the end).
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int kc = 0; kc < BQ / 16; ++kc) {
-        const v8 bd = *reinterpret_cast<const v8*>(&dOsT[(32 * nb + l32) * TSTR + 16 * kc + 8 * hh]);
-        dvacc[nb] = mfma32x32x16(pA[kc], bd, dvacc[nb]);
-        const v8 bq = *reinterpret_cast<const v8*>(&QsT[(32 * nb + l32) * TSTR + 16 * kc + 8 * hh]);
-        dkacc[nb] = mfma32x32x16(dsA[kc], bq, dkacc[nb]);
-      }
-    __syncthreads();  // the whole dS block is in LDS
-
-    // dQ_i += dS K over all 128 keys, this wave's output blocks.
+  // dQ for the query block whose dS^T sits in dSt[buf], starting at row qi0.
+  auto dq_step = [&](int buf, int qi0) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int qb = wave / NB + j * (4 / NB);
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int ch = 0; ch < BK / 16; ++ch) {
-        const v8 a = *reinterpret_cast<const v8*>(&dSs[(32 * qb + l32) * SSTR + 16 * ch + 8 * hh]);
-        acc = mfma32x32x16(a, ktf[ch], acc);
+        u32x2 part[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int row = 16 * ch + 8 * t + trrow;
+          part[t] = bwd_read_tr16(&dSt[buf][sw_off<BQ>(row, 32 * qb + trcol)]);
+        }
+        const u32x4 cat = {part[0][0], part[0][1], part[1][0], part[1][1]};
+        acc = mfma32x32x16(__builtin_bit_cast(v8, cat), ktf[ch], acc);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -222,7 +221,90 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
         if (qrow < N) unsafeAtomicAdd(dQh + (size_t)qrow * D + 32 * nb_q + l32, acc[r]);
       }
     }
+  };
+
+  const int qstart = CAUSAL ? kj0 : 0;
+  const int nsteps = (N - qstart + BQ - 1) / BQ;
+  load_step(qstart);
+  store_step(0);
+  __syncthreads();
+
+  for (int it = 0; it < nsteps; ++it) {
+    const int qi0 = qstart + it * BQ, buf = it & 1;
+    if (it + 1 < nsteps) load_step(qi0 + BQ);
+
+    const T* __restrict__ qt = Qs[buf];
+    const T* __restrict__ dt = dOs[buf];
+    // S = Q K_w^T and dP = dO V_w^T (keys on the lanes), then P and dS.
+    v8 pA[BQ / 16], dsA[BQ / 16];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int o = 32 * qb * D + rowoff[kk & 3] + 64 * (kk >> 2);
+        const v8 aq = *reinterpret_cast<const v8*>(&qt[o]);
+        const v8 ad = *reinterpret_cast<const v8*>(&dt[o]);
+        s = mfma32x32x16(aq, kf[kk], s);
+        dp = mfma32x32x16(ad, vf[kk], dp);
+      }
+      // Visibility: query qi0 + ql sees key mykey iff ql >= mykey - qi0 (causal),
+      // the query exists (ql < N - qi0) and the key exists.
+      const int lo = CAUSAL ? mykey - qi0 - 4 * hh : -(1 << 30);
+      const int hi = (key_ok ? N - qi0 : 0) - 4 * hh;
+      f32x4 lrow[4], drw[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lrow[g] = *reinterpret_cast<const f32x4*>(&Ls2[buf][32 * qb + 8 * g + 4 * hh]);
+        drw[g] = *reinterpret_cast<const f32x4*>(&Dsh[buf][32 * qb + 8 * g + 4 * hh]);
+      }
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qc = 32 * qb + 8 * (r >> 2) + (r & 3);  // query offset minus 4 hh
+        const float pe = fast_exp2(__builtin_fmaf(s[r], c, -lrow[r >> 2][r & 3]));
+        pv[r] = (qc >= lo && qc < hi) ? pe : 0.f;
+        dsv[r] = pv[r] * (dp[r] - drw[r >> 2][r & 3]);
+      }
+      pA[2 * qb] = to_v8<T>(pv);
+      pA[2 * qb + 1] = to_v8<T>(pv + 8);
+      dsA[2 * qb] = to_v8<T>(dsv);
+      dsA[2 * qb + 1] = to_v8<T>(dsv + 8);
+      // dS^T row mykey, queries 32 qb + 8 g + 4 hh + 0..3 (8-byte writes).
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        v4 q4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q4[e] = (T)dsv[4 * g + e];
+        *reinterpret_cast<u32x2*>(&dSt[buf][sw_off<BQ>(32 * wave + l32, 32 * qb + 8 * g + 4 * hh)]) =
+            __builtin_bit_cast(u32x2, q4);
+      }
+    }
+
+    // dV_w += P^T dO_i and dK_w += dS^T Q_i (scale applied at the end); the
+    // B operands come from transpose reads of the row-major tiles.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int kc = 0; kc < BQ / 16; ++kc) {
+        u32x2 pd[2], pq[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int o = sw_off<D>(16 * kc + 8 * t + trrow, 32 * nb + trcol);
+          pd[t] = bwd_read_tr16(&dt[o]);
+          pq[t] = bwd_read_tr16(&qt[o]);
+        }
+        const u32x4 cd = {pd[0][0], pd[0][1], pd[1][0], pd[1][1]};
+        const u32x4 cq = {pq[0][0], pq[0][1], pq[1][0], pq[1][1]};
+        dvacc[nb] = mfma32x32x16(pA[kc], __builtin_bit_cast(v8, cd), dvacc[nb]);
+        dkacc[nb] = mfma32x32x16(dsA[kc], __builtin_bit_cast(v8, cq), dkacc[nb]);
+      }
+
+    if (it > 0) dq_step(buf ^ 1, qi0 - BQ);  // previous block's dS^T is complete
+    if (it + 1 < nsteps) store_step(buf ^ 1);
+    __syncthreads();
   }
+  if (nsteps > 0) dq_step((nsteps - 1) & 1, qstart + (nsteps - 1) * BQ);
 
   // Write dK = scale * sum dS^T Q and dV = sum P^T dO for this wave's keys.
 #pragma unroll
@@ -262,11 +344,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkb = (a.N + BWD_BK - 1) / BWD_BK;
+  const int total = a.B * a.H * nkb;
   const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((bwd_main_kernel<T, D, CAUSAL>), dim3(a.B * a.H * nkb), dim3(BWD_THREADS), 0,
-                     s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+  hipLaunchKernelGGL((bwd_main_kernel<T, D, CAUSAL>), dim3(total), dim3(BWD_THREADS), 0, s,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.drow,
-                     a.dq_acc, static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, nkb, a.scale, c);
+                     a.dq_acc, static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, nkb, total,
+                     a.scale, c);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long n8 = rows * D / 8;
