@@ -27,6 +27,8 @@ fa_status check_common(int B, int H, int N, int d, float scale, fa_dtype dt) {
   if (elems > kMaxElems) return FA_ERR_SHAPE;
   // every kernel grid is at most one workgroup per 64 rows or per 32 row-chunks
   if ((long long)B * H * ((N + 63) / 64) > kMaxGrid) return FA_ERR_SHAPE;
+  // per-head element offsets are 32-bit inside the kernels
+  if ((long long)N * d >= (1LL << 31)) return FA_ERR_SHAPE;
   if (elems / 8 / 256 + 1 > kMaxGrid) return FA_ERR_SHAPE;
   return FA_OK;
 }

@@ -26,21 +26,25 @@
 //
 // Pipelining in bwd_main: the next query block's Q, dO, L and D are loaded
 // into registers while the current block is computed; tiles and the dS^T
-// block are double-buffered in LDS, and the dQ product of a block runs one
-// step later, so each step needs a single barrier.
+// block are double-buffered in LDS, and the dQ product of a block runs at the
+// start of the next step, so each step needs a single barrier.  The dQ
+// atomics are issued before the step's matrix work: vector-memory counters
+// track stores and atomics together with loads, so the wait for the
+// prefetched tile at the end of the step would otherwise also wait for a
+// fresh round trip of every atomic.
 //
 // LDS layout: row-major tiles without padding, 16-byte chunk c of row r
-// stored at chunk c ^ sw(r), sw(r) = 2 (r mod 4) + (r / 4 mod 2).  Eight
-// consecutive rows then hit eight different chunks (16-byte row reads are
-// conflict-free) and four consecutive rows hit four different chunk pairs
-// (transpose reads are conflict-free).
+// stored at chunk c ^ sw(r).  For rows of 8 or more chunks sw(r) =
+// 2 (r mod 4) + (r / 4 mod 2): eight consecutive rows then hit eight
+// different chunks (16-byte row reads are conflict-free) and four consecutive
+// rows hit four different chunk pairs (transpose reads are conflict-free).
+// Rows of 4 chunks (the dS^T tile at 32 queries per step) use a 2-bit swizzle
+// with the same transpose-read property.
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 
-constexpr int BWD_BK = 128;  // keys per workgroup (4 waves x 32)
-constexpr int BWD_BQ = 64;   // query rows per step
 constexpr int BWD_THREADS = 256;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -51,12 +55,20 @@ __device__ __forceinline__ u32x2 bwd_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Chunk swizzle of row r for rows of at least 8 chunks (3 bits) and for rows
+// of 4 chunks (2 bits: r bit 1 spreads the rows a transpose read touches,
+// r bit 2 halves the conflicts of column writes).
+template <int ROWLEN>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(ROWLEN == 32 || ROWLEN % 64 == 0, "swizzle defined for 4 or >= 8 chunks per row");
+  if (ROWLEN == 32) return (r & 2) | ((r >> 2) & 1);
+  return ((r & 3) << 1) | ((r >> 2) & 1);
+}
 
 // Element offset of (row, col) in a swizzled row-major tile of ROWLEN elements.
 template <int ROWLEN>
 __device__ __forceinline__ int sw_off(int row, int col) {
-  return row * ROWLEN + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+  return row * ROWLEN + ((((col >> 3) ^ swz<ROWLEN>(row)) << 3) | (col & 7));
 }
 
 // ---------------------------------------------------------------- kernel 1
@@ -86,7 +98,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 }
 
 // ---------------------------------------------------------------- kernel 2
-template <typename T, int D, bool CAUSAL>
+// KH = 32-key groups per wave (the workgroup owns BK = 128 KH keys), BQ =
+// query rows per step.  Larger BK means fewer dQ atomics in total (each
+// element of dQ receives one atomic add per key block).
+template <typename T, int D, bool CAUSAL, int KH, int BQ>
 __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ drow,
@@ -94,15 +109,16 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
     int total, float scale, float c) {
   using v8 = typename Vec<T>::v8;
   using v4 = typename Vec<T>::v4;
-  constexpr int BK = BWD_BK, BQ = BWD_BQ;
+  constexpr int BK = 128 * KH;
   constexpr int NB = D / 32;          // 32-column blocks of D
   constexpr int QB = BQ / 32;         // 32-row blocks of a query step
+  constexpr int NDQ = NB * QB;        // 32x32 dQ output blocks per step
   constexpr int CH = BQ * D / 8;      // 16-byte chunks per Q (or dO) tile
-  constexpr int CPT = CH / BWD_THREADS;
-  static_assert(CH % BWD_THREADS == 0, "tile chunks must divide evenly");
+  constexpr int CPT = (CH + BWD_THREADS - 1) / BWD_THREADS;
   __shared__ __attribute__((aligned(16))) T Qs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) T dOs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) T dSt[2][BK * BQ];  // dS^T: [key][query]
+  __shared__ __attribute__((aligned(16))) T Kt[BK * D];       // this block's keys
   __shared__ __attribute__((aligned(16))) float Ls2[2][BQ];
   __shared__ __attribute__((aligned(16))) float Dsh[2][BQ];
 
@@ -124,33 +140,42 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
   float* __restrict__ dQh = dq_acc + hoff;
 
   const int kj0 = kblk * BK;
-  const int mykey = kj0 + 32 * wave + l32;  // key this lane owns in S, dP, dS
-  const bool key_ok = mykey < N;
-
-  // K_w and V_w as B operands of S = Q K^T and dP = dO V^T.
-  v8 kf[D / 16], vf[D / 16];
+  const int kw0 = kj0 + 32 * KH * wave;  // first key of this wave
+  int mykey[KH];                         // keys this lane owns in S, dP, dS
+  bool key_ok[KH];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    kf[kk] = key_ok ? ld16<v8>(Kh + (size_t)mykey * D + 16 * kk + 8 * hh) : v8{};
-    vf[kk] = key_ok ? ld16<v8>(Vh + (size_t)mykey * D + 16 * kk + 8 * hh) : v8{};
+  for (int h = 0; h < KH; ++h) {
+    mykey[h] = kw0 + 32 * h + l32;
+    key_ok[h] = mykey[h] < N;
   }
-  // K as the B operand of dQ = dS K, in the key order the transpose read of
-  // dS^T produces: element e of lane half hh is key 8 (e / 4) + 4 hh + (e % 4)
-  // of each 16-key chunk; column 32 nb_q + l32.
-  constexpr int PER_WAVE = NB * QB / 4;  // dQ output blocks per wave
-  const int nb_q = wave % NB;
-  v8 ktf[BK / 16];
-#pragma unroll
-  for (int ch = 0; ch < BK / 16; ++ch)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = kj0 + 16 * ch + 8 * (e >> 2) + 4 * hh + (e & 3);
-      ktf[ch][e] = (key < N) ? Kh[(size_t)key * D + 32 * nb_q + l32] : (T)0.f;
-    }
 
-  f32x16 dvacc[NB], dkacc[NB];
+  // K_w and V_w as B operands of S = Q K^T and dP = dO V^T.  With two key
+  // groups per wave the register file holds the dK / dV accumulators and V_w
+  // only, and the K_w operand is read from the block's K tile in LDS instead.
+  constexpr bool KF_LDS = KH >= 2;
+  v8 kf[KF_LDS ? 1 : KH][D / 16], vf[KH][D / 16];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) { dvacc[i] = f32x16{}; dkacc[i] = f32x16{}; }
+  for (int h = 0; h < KH; ++h)
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      if (!KF_LDS)
+        kf[h][kk] = key_ok[h] ? ld16<v8>(Kh + (size_t)mykey[h] * D + 16 * kk + 8 * hh) : v8{};
+      vf[h][kk] = key_ok[h] ? ld16<v8>(Vh + (size_t)mykey[h] * D + 16 * kk + 8 * hh) : v8{};
+    }
+  // The block's K rows in LDS (swizzled): the B operand of dQ = dS K comes
+  // from transpose reads of it.  Rows past the end are zero.
+  for (int e = tid; e < BK * D / 8; e += BWD_THREADS) {
+    const int row = e / (D / 8), col = 8 * (e % (D / 8));
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (kj0 + row < N) val = *reinterpret_cast<const u32x4*>(Kh + (size_t)(kj0 + row) * D + col);
+    *reinterpret_cast<u32x4*>(&Kt[sw_off<D>(row, col)]) = val;
+  }
+
+  f32x16 dvacc[KH][NB], dkacc[KH][NB];
+#pragma unroll
+  for (int h = 0; h < KH; ++h)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) { dvacc[h][i] = f32x16{}; dkacc[h][i] = f32x16{}; }
 
   // Per-lane LDS offsets (elements).
   //  * 16-byte row reads of Q / dO (A operands of S and dP): row 32 qb + l32,
@@ -159,13 +184,13 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
   int rowoff[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) rowoff[m] = sw_off<D>(l32, 16 * m + 8 * hh);
-  //  * transpose reads of Q / dO (B operands of dK / dV): rows 16 kc + 8 t +
-  //    4 hh + li / 4, columns 32 nb + 16 (grp mod 2) + 4 (li mod 4).
+  //  * transpose reads (B operands of dK / dV from the Q / dO tiles, of dQ from
+  //    the K tile, and the A operand of dQ from the dS^T tile): lane li of
+  //    16-lane group grp addresses row 16 c + 8 t + trrow, column 32 b + trcol.
+  //    In every case the reduction index (rows) comes out in the order the
+  //    32x32 accumulator layout hands values to the other operand.
   const int trrow = 4 * hh + (li >> 2);
   const int trcol = 16 * (grp & 1) + 4 * (li & 3);
-  //  * transpose reads of dS^T (A operand of dQ): rows (keys) 16 ch + 8 t +
-  //    4 hh + li / 4, columns (queries) 32 qb + 16 (grp mod 2) + 4 (li mod 4).
-  // Swizzle of a row depends only on row mod 8 = 8 t + trrow mod 8 = trrow + 8t.
 
   u32x4 qpre[CPT], dpre[CPT];
   float lpre = 0.f, dpre_row = 0.f;
@@ -173,10 +198,12 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int e = tid + i * BWD_THREADS;
-      const int row = min(qi0 + e / (D / 8), N - 1), c8 = e % (D / 8);
-      const size_t off = (size_t)row * D + 8 * c8;
-      qpre[i] = *reinterpret_cast<const u32x4*>(Qh + off);
-      dpre[i] = *reinterpret_cast<const u32x4*>(dOh + off);
+      if (CH % BWD_THREADS == 0 || e < CH) {
+        const int row = min(qi0 + e / (D / 8), N - 1), c8 = e % (D / 8);
+        const size_t off = (size_t)row * D + 8 * c8;
+        qpre[i] = *reinterpret_cast<const u32x4*>(Qh + off);
+        dpre[i] = *reinterpret_cast<const u32x4*>(dOh + off);
+      }
     }
     if (tid < BQ) {
       const int qrow = qi0 + tid;
@@ -188,9 +215,11 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int e = tid + i * BWD_THREADS;
-      const int row = e / (D / 8), col = 8 * (e % (D / 8));
-      *reinterpret_cast<u32x4*>(&Qs[buf][sw_off<D>(row, col)]) = qpre[i];
-      *reinterpret_cast<u32x4*>(&dOs[buf][sw_off<D>(row, col)]) = dpre[i];
+      if (CH % BWD_THREADS == 0 || e < CH) {
+        const int row = e / (D / 8), col = 8 * (e % (D / 8));
+        *reinterpret_cast<u32x4*>(&Qs[buf][sw_off<D>(row, col)]) = qpre[i];
+        *reinterpret_cast<u32x4*>(&dOs[buf][sw_off<D>(row, col)]) = dpre[i];
+      }
     }
     if (tid < BQ) {
       Ls2[buf][tid] = lpre;
@@ -198,27 +227,40 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
     }
   };
 
-  // dQ for the query block whose dS^T sits in dSt[buf], starting at row qi0.
+  // dQ for the query block whose dS^T sits in dSt[buf], starting at row qi0:
+  // 32x32 output blocks wave, wave + 4, ... of the BQ x D block.
   auto dq_step = [&](int buf, int qi0) {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int qb = wave / NB + j * (4 / NB);
+    for (int blk = wave; blk < NDQ; blk += 4) {
+      const int nb = blk % NB, qb = blk / NB;
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int ch = 0; ch < BK / 16; ++ch) {
-        u32x2 part[2];
+        u32x2 pa[2], pk[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int row = 16 * ch + 8 * t + trrow;
-          part[t] = bwd_read_tr16(&dSt[buf][sw_off<BQ>(row, 32 * qb + trcol)]);
+          pa[t] = bwd_read_tr16(&dSt[buf][sw_off<BQ>(row, 32 * qb + trcol)]);
+          pk[t] = bwd_read_tr16(&Kt[sw_off<D>(row, 32 * nb + trcol)]);
         }
-        const u32x4 cat = {part[0][0], part[0][1], part[1][0], part[1][1]};
-        acc = mfma32x32x16(__builtin_bit_cast(v8, cat), ktf[ch], acc);
+        const u32x4 ca = {pa[0][0], pa[0][1], pa[1][0], pa[1][1]};
+        const u32x4 ck = {pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+        acc = mfma32x32x16(__builtin_bit_cast(v8, ca), __builtin_bit_cast(v8, ck), acc);
       }
+      // Element (row qrow, column 32 nb + l32) of this head's dQ accumulator,
+      // addressed by a 32-bit offset from the head base (a head holds fewer
+      // than 2^31 elements, which the host checks).
+      const int off0 = (qi0 + 32 * qb + 4 * hh) * D + 32 * nb + l32;
+      if (qi0 + BQ <= N) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qrow = qi0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (qrow < N) unsafeAtomicAdd(dQh + (size_t)qrow * D + 32 * nb_q + l32, acc[r]);
+        for (int r = 0; r < 16; ++r)
+          unsafeAtomicAdd(dQh + off0 + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = qi0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (qrow < N) unsafeAtomicAdd(dQh + off0 + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
+        }
       }
     }
   };
@@ -231,76 +273,110 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
 
   for (int it = 0; it < nsteps; ++it) {
     const int qi0 = qstart + it * BQ, buf = it & 1;
+    // The previous block's dQ first: its atomics then drain while this block
+    // is computed (the wait for the prefetched tile below also covers them).
+    if (it > 0) dq_step(buf ^ 1, qi0 - BQ);
     if (it + 1 < nsteps) load_step(qi0 + BQ);
 
     const T* __restrict__ qt = Qs[buf];
     const T* __restrict__ dt = dOs[buf];
-    // S = Q K_w^T and dP = dO V_w^T (keys on the lanes), then P and dS.
-    v8 pA[BQ / 16], dsA[BQ / 16];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int o = 32 * qb * D + rowoff[kk & 3] + 64 * (kk >> 2);
-        const v8 aq = *reinterpret_cast<const v8*>(&qt[o]);
-        const v8 ad = *reinterpret_cast<const v8*>(&dt[o]);
-        s = mfma32x32x16(aq, kf[kk], s);
-        dp = mfma32x32x16(ad, vf[kk], dp);
-      }
+    for (int h = 0; h < KH; ++h) {
+      // S = Q K_w^T and dP = dO V_w^T (keys on the lanes), then P and dS.
+      v8 pA[BQ / 16], dsA[BQ / 16];
+      const bool need_mask = (CAUSAL && qi0 < kw0 + 32 * h + 31) || (qi0 + BQ > N) ||
+                             (kw0 + 32 * h + 32 > N);
       // Visibility: query qi0 + ql sees key mykey iff ql >= mykey - qi0 (causal),
       // the query exists (ql < N - qi0) and the key exists.
-      const int lo = CAUSAL ? mykey - qi0 - 4 * hh : -(1 << 30);
-      const int hi = (key_ok ? N - qi0 : 0) - 4 * hh;
-      f32x4 lrow[4], drw[4];
+      const int lo = CAUSAL ? mykey[h] - qi0 - 4 * hh : -(1 << 30);
+      const int hi = (key_ok[h] ? N - qi0 : 0) - 4 * hh;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lrow[g] = *reinterpret_cast<const f32x4*>(&Ls2[buf][32 * qb + 8 * g + 4 * hh]);
-        drw[g] = *reinterpret_cast<const f32x4*>(&Dsh[buf][32 * qb + 8 * g + 4 * hh]);
+      for (int qb = 0; qb < QB; ++qb) {
+        // Phase 1: S = Q K_w^T, then P (kept only in the storage type).
+        f32x16 sa = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int o = 32 * qb * D + rowoff[kk & 3] + 64 * (kk >> 2);
+          const v8 aq = *reinterpret_cast<const v8*>(&qt[o]);
+          const v8 bk = KF_LDS ? *reinterpret_cast<const v8*>(
+                                     &Kt[(32 * KH * wave + 32 * h) * D + rowoff[kk & 3] + 64 * (kk >> 2)])
+                               : kf[KF_LDS ? 0 : h][kk];
+          sa = mfma32x32x16(aq, bk, sa);
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float pv[8];
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls2[buf][32 * qb + 16 * hf + 8 * g2 + 4 * hh]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * hf + 4 * g2 + e;
+              float pe = fast_exp2(__builtin_fmaf(sa[r], c, -l4[e]));
+              if (need_mask) {
+                const int qc = 32 * qb + 8 * (r >> 2) + (r & 3);  // query offset minus 4 hh
+                pe = (qc >= lo && qc < hi) ? pe : 0.f;
+              }
+              pv[4 * g2 + e] = pe;
+            }
+          }
+          pA[2 * qb + hf] = to_v8<T>(pv);
+        }
+        // Phase 2: dP = dO V_w^T, then dS = P o (dP - D) with P as rounded for
+        // the P^T dO product (dS is rounded to the storage type as well).
+        f32x16 dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int o = 32 * qb * D + rowoff[kk & 3] + 64 * (kk >> 2);
+          const v8 ad = *reinterpret_cast<const v8*>(&dt[o]);
+          dp = mfma32x32x16(ad, vf[h][kk], dp);
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float dsv[8];
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dsh[buf][32 * qb + 16 * hf + 8 * g2 + 4 * hh]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * hf + 4 * g2 + e;
+              dsv[4 * g2 + e] = (float)pA[2 * qb + hf][4 * g2 + e] * (dp[r] - d4[e]);
+            }
+          }
+          dsA[2 * qb + hf] = to_v8<T>(dsv);
+          // dS^T row of this lane's key, queries 32 qb + 8 g + 4 hh + 0..3 (8-byte writes).
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            v4 q4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q4[e] = dsA[2 * qb + hf][4 * g2 + e];
+            *reinterpret_cast<u32x2*>(&dSt[buf][sw_off<BQ>(32 * KH * wave + 32 * h + l32,
+                                                           32 * qb + 16 * hf + 8 * g2 + 4 * hh)]) =
+                __builtin_bit_cast(u32x2, q4);
+          }
+        }
       }
-      float pv[16], dsv[16];
+
+      // dV_w += P^T dO_i and dK_w += dS^T Q_i (scale applied at the end); the
+      // B operands come from transpose reads of the row-major tiles.
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qc = 32 * qb + 8 * (r >> 2) + (r & 3);  // query offset minus 4 hh
-        const float pe = fast_exp2(__builtin_fmaf(s[r], c, -lrow[r >> 2][r & 3]));
-        pv[r] = (qc >= lo && qc < hi) ? pe : 0.f;
-        dsv[r] = pv[r] * (dp[r] - drw[r >> 2][r & 3]);
-      }
-      pA[2 * qb] = to_v8<T>(pv);
-      pA[2 * qb + 1] = to_v8<T>(pv + 8);
-      dsA[2 * qb] = to_v8<T>(dsv);
-      dsA[2 * qb + 1] = to_v8<T>(dsv + 8);
-      // dS^T row mykey, queries 32 qb + 8 g + 4 hh + 0..3 (8-byte writes).
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        v4 q4;
+        for (int kc = 0; kc < BQ / 16; ++kc) {
+          u32x2 pd[2], pq[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) q4[e] = (T)dsv[4 * g + e];
-        *reinterpret_cast<u32x2*>(&dSt[buf][sw_off<BQ>(32 * wave + l32, 32 * qb + 8 * g + 4 * hh)]) =
-            __builtin_bit_cast(u32x2, q4);
-      }
+          for (int t = 0; t < 2; ++t) {
+            const int o = sw_off<D>(16 * kc + 8 * t + trrow, 32 * nb + trcol);
+            pd[t] = bwd_read_tr16(&dt[o]);
+            pq[t] = bwd_read_tr16(&qt[o]);
+          }
+          const u32x4 cd = {pd[0][0], pd[0][1], pd[1][0], pd[1][1]};
+          const u32x4 cq = {pq[0][0], pq[0][1], pq[1][0], pq[1][1]};
+          dvacc[h][nb] = mfma32x32x16(pA[kc], __builtin_bit_cast(v8, cd), dvacc[h][nb]);
+          dkacc[h][nb] = mfma32x32x16(dsA[kc], __builtin_bit_cast(v8, cq), dkacc[h][nb]);
+        }
     }
 
-    // dV_w += P^T dO_i and dK_w += dS^T Q_i (scale applied at the end); the
-    // B operands come from transpose reads of the row-major tiles.
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int kc = 0; kc < BQ / 16; ++kc) {
-        u32x2 pd[2], pq[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int o = sw_off<D>(16 * kc + 8 * t + trrow, 32 * nb + trcol);
-          pd[t] = bwd_read_tr16(&dt[o]);
-          pq[t] = bwd_read_tr16(&qt[o]);
-        }
-        const u32x4 cd = {pd[0][0], pd[0][1], pd[1][0], pd[1][1]};
-        const u32x4 cq = {pq[0][0], pq[0][1], pq[1][0], pq[1][1]};
-        dvacc[nb] = mfma32x32x16(pA[kc], __builtin_bit_cast(v8, cd), dvacc[nb]);
-        dkacc[nb] = mfma32x32x16(dsA[kc], __builtin_bit_cast(v8, cq), dkacc[nb]);
-      }
-
-    if (it > 0) dq_step(buf ^ 1, qi0 - BQ);  // previous block's dS^T is complete
     if (it + 1 < nsteps) store_step(buf ^ 1);
     __syncthreads();
   }
@@ -308,15 +384,17 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
 
   // Write dK = scale * sum dS^T Q and dV = sum P^T dO for this wave's keys.
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int h = 0; h < KH; ++h)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kj0 + 32 * wave + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (key < N) {
-        dK[hoff + (size_t)key * D + 32 * nb + l32] = (T)(dkacc[nb][r] * scale);
-        dV[hoff + (size_t)key * D + 32 * nb + l32] = (T)dvacc[nb][r];
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kw0 + 32 * h + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key < N) {
+          dK[hoff + (size_t)key * D + 32 * nb + l32] = (T)(dkacc[h][nb][r] * scale);
+          dV[hoff + (size_t)key * D + 32 * nb + l32] = (T)dvacc[h][nb][r];
+        }
       }
-    }
 }
 
 // ---------------------------------------------------------------- kernel 3
@@ -334,6 +412,27 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ a
   st16<v8>(dQ + 8 * i, r);
 }
 
+// Two shapes of the main kernel: 256 keys per workgroup halves the dQ atomics
+// (the dominant cost at long sequence lengths) but makes each workgroup twice
+// as long, which a short causal sequence cannot balance across the CUs.  The
+// wider shape is used when it still yields at least four workgroups per CU.
+#ifndef FA_BWD_FORCE_KH
+#define FA_BWD_FORCE_KH 0
+#endif
+
+template <typename T, int D, bool CAUSAL, int KH, int BQ>
+static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t s) {
+  const int nkb = (a.N + 128 * KH - 1) / (128 * KH);
+  const int total = a.B * a.H * nkb;
+  const float c = a.scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((bwd_main_kernel<T, D, CAUSAL, KH, BQ>), dim3(total), dim3(BWD_THREADS), 0, s,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.drow,
+                     a.dq_acc, static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, nkb, total,
+                     a.scale, c);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.H * a.N;
@@ -343,15 +442,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
                      a.dq_acc, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nkb = (a.N + BWD_BK - 1) / BWD_BK;
-  const int total = a.B * a.H * nkb;
-  const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((bwd_main_kernel<T, D, CAUSAL>), dim3(total), dim3(BWD_THREADS), 0, s,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.drow,
-                     a.dq_acc, static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, nkb, total,
-                     a.scale, c);
-  e = hipGetLastError();
+  const long wide_blocks = (long)a.B * a.H * ((a.N + 255) / 256);
+  const bool wide = FA_BWD_FORCE_KH ? FA_BWD_FORCE_KH == 2 : wide_blocks >= 4L * 256;
+  e = wide ? launch_bwd_main<T, D, CAUSAL, 2, 32>(a, s) : launch_bwd_main<T, D, CAUSAL, 1, 64>(a, s);
   if (e != hipSuccess) return e;
   const long n8 = rows * D / 8;
   hipLaunchKernelGGL((bwd_dq_kernel<T>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,

@@ -58,3 +58,34 @@ def test_bwd_full_size_workload():
         ref = oracle.attn_bwd(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
         for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
             check_rel_norm(host64(g[b, h]), r, w.dtype, f"{name} head ({b},{h})")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bwd_wide_key_blocks(causal, d, dtype):
+    """Enough heads that the launcher picks 256 keys per workgroup (B H ceil(N/256) >= 1024);
+    N = 500 leaves a ragged last key block."""
+    B, H, N = 2, 256, 500
+    seed = 8500 + d + (1 if causal else 0)
+    announce(f"bwd wide blocks B{B} H{H} N{N} d{d} causal={causal} {dtype} seed={seed}")
+    q, k, v, do = attention_inputs(B, H, N, d, dtype, seed, "cpu", with_dout=True)
+    scale = d ** -0.5
+    dq, dk, dv = run_fwd_bwd(*(t.to(DEV) for t in (q, k, v, do)), scale, causal)
+    for b, h in [(0, 0), (0, 131), (1, 255)]:
+        ref = oracle.attn_bwd(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+        for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+            check_rel_norm(host64(g[b, h]), r, dtype, f"{name} head ({b},{h})")
+
+
+def test_bwd_at_bench_shape():
+    """The backward launch the benchmark times: B1 H32 N8192 d128 bf16 causal, Q x2."""
+    from synth_inputs import FWD_8K as w
+    announce(f"bwd at the benchmark shape {w.name} seed={w.seed}")
+    q, k, v, do = attention_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, "cpu", q_mult=w.q_mult,
+                                   with_dout=True)
+    dq, dk, dv = run_fwd_bwd(*(t.to(DEV) for t in (q, k, v, do)), w.scale, w.causal)
+    for b, h in [(0, 0), (0, w.H - 1)]:
+        ref = oracle.attn_bwd(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
+        for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+            check_rel_norm(host64(g[b, h]), r, w.dtype, f"{name} head ({b},{h})")
