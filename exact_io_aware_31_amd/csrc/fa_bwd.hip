@@ -280,6 +280,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
 
     const T* __restrict__ qt = Qs[buf];
     const T* __restrict__ dt = dOs[buf];
+    // Let the scheduler interleave the LDS reads with the matrix products.
+    __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
     for (int h = 0; h < KH; ++h) {
       // S = Q K_w^T and dP = dO V_w^T (keys on the lanes), then P and dS.
