@@ -66,8 +66,25 @@ def build_library(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_kernel_stubs(lib: str) -> None:
+    """Fail if a kernel's host-side launch stub is undefined.
+
+    When the host pass cannot analyse a kernel body (for example a target
+    builtin called directly in it rather than through a __device__ helper),
+    hipcc drops the kernel's host stub without an error; the library then
+    links but cannot be loaded.  Catch that at build time."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    r = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        return  # no nm available: skip the check rather than fail the build
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from libfa.so: " + ", ".join(missing))
 
 
 if __name__ == "__main__":

@@ -21,9 +21,14 @@
 //     layout with a consistent permutation of the reduction index.  The A
 //     operand V^T is read from the row-major V tile with the LDS transpose
 //     read (ds_read_b64_tr_b16), so V is never transposed in memory.
-//   * K and V tiles are double-buffered in LDS; the next tile's global loads
-//     are issued before the current tile is computed, so their latency hides
-//     behind the matrix work; one barrier per tile.
+//   * K and V tiles reach LDS by direct global-to-LDS loads
+//     (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS
+//     base + 16 * lane), two tiles ahead of their use, in a three-deep ring.
+//     No registers hold staged data and no LDS store instructions are issued;
+//     each wave waits for its own loads before the tile's barrier.  Tiles are
+//     stored unpadded with 16-byte chunk c of row r at chunk c ^ sw(r), which
+//     keeps the 16-byte row reads and the transpose reads conflict-free; the
+//     loading lane picks the global chunk that belongs in its LDS slot.
 //   * Running max in log2 units with log2(e) folded into the scale (v_exp_f32).
 //     The output is rescaled only when a row's maximum grows by more than
 //     2^8: until then the stale maximum is kept as the reference, which leaves
@@ -53,6 +58,12 @@ constexpr int FWD_BR = FWD_NW * 32 * FWD_QG;
 constexpr int FWD_BC = 64;
 constexpr float FWD_RESCALE_SLACK = 8.0f;  // log2 units
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+#define FWD_VMCNT(n) ((((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14)))
+// ... and additionally until every LDS operation of this wave has completed.
+#define FWD_VMCNT_LGKM0(n) (FWD_VMCNT(n) & ~(15 << 8))
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
@@ -64,6 +75,46 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base must be wave-uniform).
+__device__ __forceinline__ void lds_load16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+// Wait on this wave's outstanding counters.  The empty asm statements with a
+// memory clobber keep the compiler from moving LDS accesses across the wait
+// (the builtin alone is not a memory barrier to the compiler).
+template <int IMM>
+__device__ __forceinline__ void wait_counts() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(IMM);
+  asm volatile("" ::: "memory");
+}
+// Workgroup barrier without the memory fence of __syncthreads() (which would
+// also wait for the loads of the tile after next); the memory clobbers keep
+// every LDS access on its side of the barrier.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Chunk swizzle of tile row r (rows of D two-byte elements): 256-byte rows
+// use sw(r) = 4 (r mod 4) + (r / 4 mod 4), 128-byte rows sw(r) = r / 2 mod 8.
+// Either way sixteen consecutive rows read at one logical chunk touch every
+// bank once, and the 4-row x 32-byte footprint of a transpose read is
+// conflict-free.  The swizzle depends on r mod 16 only.
+template <int D>
+__device__ __forceinline__ int fwd_swz(int r) {
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
+}
+// Element offset of (row, col) in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int fwd_toff(int row, int col) {
+  return row * D + ((((col >> 3) ^ fwd_swz<D>(row)) << 3) | (col & 7));
+}
+
 template <typename T, int D, bool CAUSAL, int NW, int QG>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -72,12 +123,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   using v4 = typename Vec<T>::v4;
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32 * QG, BC = FWD_BC;
-  constexpr int KSTR = D + 8;   // K rows: 16-byte pad, conflict-free 16-byte row reads
-  constexpr int VSTR = D + 16;  // V rows: 32-byte pad, conflict-free transpose reads
-  constexpr int CH = BC * D / 8;                 // 16-byte chunks per tile
-  constexpr int CPT = (CH + NT - 1) / NT;        // chunks per thread
-  __shared__ __attribute__((aligned(16))) T Ks[2][BC * KSTR];
-  __shared__ __attribute__((aligned(16))) T Vs[2][BC * VSTR];
+  constexpr int RPS = 512 / D;                  // tile rows per 1 KiB load segment
+  constexpr int NSEG = BC * D * 2 / 1024;       // segments per tile
+  constexpr int SPW = NSEG / NW;                // segments each wave loads
+  static_assert(NSEG % NW == 0 && NT == 512, "tile segments split evenly over the waves");
+  // Three-deep ring of K and V tiles (separate arrays, so every access names
+  // its buffer statically and the compiler sees which loads it depends on).
+  __shared__ __attribute__((aligned(1024))) T K0[BC * D], K1[BC * D], K2[BC * D];
+  __shared__ __attribute__((aligned(1024))) T V0[BC * D], V1[BC * D], V2[BC * D];
 
   // Work item: XCD-local heads, heaviest causal query blocks first.
   const int p = blockIdx.x;
@@ -85,7 +138,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   const int bh = w / nqb;
   const int qb = CAUSAL ? nqb - 1 - (w % nqb) : (w % nqb);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform_int(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const size_t hoff = (size_t)bh * N * D;
   const T* __restrict__ Qh = Q + hoff;
@@ -118,48 +172,62 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   const int kv_end = CAUSAL ? min(N, (qb + 1) * BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  // Tile staging: thread moves chunks tid, tid + NT, ... of the K and V tiles.
-  // Rows past the end are clamped to row N-1: those keys are masked to -inf
-  // before the softmax, so their probabilities (and their V rows' weight) are 0.
-  u32x4 kpre[CPT], vpre[CPT];
-  auto load_tile = [&](int kb) {
+  // Tile loads: wave w fills segments w SPW .. w SPW + SPW - 1 of a tile; lane
+  // l of segment g fills LDS chunk slot l of the segment, i.e. tile row
+  // g RPS + l / (D / 8), physical chunk l mod (D / 8), with the logical chunk
+  // that the swizzle puts there.  Rows past the end are clamped to row N-1:
+  // those keys are masked to -inf before the softmax, so their probabilities
+  // (and their V rows' weight) are 0.
+  auto load_tile = [&](const T* __restrict__ src, T* dst, int kb) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int e = tid + i * NT;
-      if (CH % NT == 0 || e < CH) {
-        const int row = min(kb + e / (D / 8), N - 1), c8 = e % (D / 8);
-        const size_t off = (size_t)row * D + 8 * c8;
-        kpre[i] = *reinterpret_cast<const u32x4*>(Kh + off);
-        vpre[i] = *reinterpret_cast<const u32x4*>(Vh + off);
-      }
+    for (int i = 0; i < SPW; ++i) {
+      const int g = wave * SPW + i;
+      const int row = g * RPS + lane / (D / 8);
+      const int chunk = (lane % (D / 8)) ^ fwd_swz<D>(row);
+      const T* gp = src + (size_t)min(kb + row, N - 1) * D + 8 * chunk;
+      lds_load16(gp, dst + g * 512);
     }
   };
-  auto store_tile = [&](int buf) {
+  // Per-lane element offsets of the operand reads (the swizzle depends on the
+  // row mod 16 only, so they hold for every 16- or 32-row block of a tile):
+  //  * K rows (A operand of S^T = K Q^T): row l32, columns 16 kk + 8 hh.
+  //  * V^T (A operand of O^T += V^T P^T) by transpose reads: lane i of 16-lane
+  //    group G addresses key 8 t + 4 hh + i / 4, columns 32 nb + 16 (G mod 2)
+  //    + 4 (i mod 4).
+  int koff[D / 16];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int e = tid + i * NT;
-      if (CH % NT == 0 || e < CH) {
-        const int row = e / (D / 8), c8 = e % (D / 8);
-        *reinterpret_cast<u32x4*>(&Ks[buf][row * KSTR + 8 * c8]) = kpre[i];
-        *reinterpret_cast<u32x4*>(&Vs[buf][row * VSTR + 8 * c8]) = vpre[i];
-      }
-    }
-  };
-
-  // Per-lane offsets of the transpose reads that build the V^T operand:
-  // lane i of 16-lane group G addresses key 4 hh + i / 4 (+ 8 t), columns
-  // 16 (G mod 2) + 4 (i mod 4) (+ 32 nb).
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = fwd_toff<D>(l32, 16 * kk + 8 * hh);
   const int grp = lane >> 4, li = lane & 15;
-  const int voff = (4 * hh + (li >> 2)) * VSTR + 16 * (grp & 1) + 4 * (li & 3);
+  int voff[2][D / 32];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+      voff[t][nb] = fwd_toff<D>(8 * t + 4 * hh + (li >> 2), 32 * nb + 16 * (grp & 1) + 4 * (li & 3));
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // Tiles 0 and 1 in flight; wait for tile 0 (vmcnt counts this wave's loads).
+  load_tile(Kh, K0, 0);
+  load_tile(Vh, V0, 0);
+  if (ntiles > 1) {
+    load_tile(Kh, K1, BC);
+    load_tile(Vh, V1, BC);
+    wait_counts<FWD_VMCNT_LGKM0(2 * SPW)>();
+  } else {
+    wait_counts<FWD_VMCNT_LGKM0(0)>();
+  }
+  // A bare barrier: the waits above already cover what it must publish (a
+  // fenced barrier would also wait for the loads of the tile after next).
+  bare_barrier();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int kb = j * BC, buf = j & 1;
-    if (j + 1 < ntiles) load_tile(kb + BC);  // in flight while tile j is computed
-
+  // One tile: tile j+2 starts loading into the buffer tile j-1 used, tile j is
+  // computed, and before the barrier this wave's loads of tile j+1 are done.
+  auto tile_step = [&](int j, const T* __restrict__ kt, const T* __restrict__ vt, T* kn, T* vn) {
+    const int kb = j * BC;
+    const bool more = j + 2 < ntiles;
+    if (more) {
+      load_tile(Kh, kn, kb + 2 * BC);
+      load_tile(Vh, vn, kb + 2 * BC);
+    }
     bool active[QG];
     bool any_active = false;
 #pragma unroll
@@ -168,8 +236,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
       any_active |= active[g];
     }
     if (any_active) {
-      const T* __restrict__ kt = Ks[buf];
-      const T* __restrict__ vt = Vs[buf];
       // S^T = K Q^T for BC/32 blocks of 32 keys; the blocks are interleaved so
       // consecutive MFMAs are independent, and each K operand is read from LDS
       // one step before the MFMA that uses it.
@@ -178,17 +244,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
       for (int g = 0; g < QG; ++g)
 #pragma unroll
         for (int sb = 0; sb < BC / 32; ++sb) sacc[g][sb] = f32x16{};
-      const T* krow = kt + l32 * KSTR + 8 * hh;
       v8 ka[2][BC / 32];
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb)
-        ka[0][sb] = *reinterpret_cast<const v8*>(krow + 32 * sb * KSTR);
+        ka[0][sb] = *reinterpret_cast<const v8*>(kt + 32 * sb * D + koff[0]);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         if (kk + 1 < D / 16) {
 #pragma unroll
           for (int sb = 0; sb < BC / 32; ++sb)
-            ka[(kk + 1) & 1][sb] = *reinterpret_cast<const v8*>(krow + 32 * sb * KSTR + 16 * (kk + 1));
+            ka[(kk + 1) & 1][sb] = *reinterpret_cast<const v8*>(kt + 32 * sb * D + koff[kk + 1]);
         }
 #pragma unroll
         for (int sb = 0; sb < BC / 32; ++sb)
@@ -259,9 +324,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
       for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
         for (int kc = 0; kc < BC / 16; ++kc) {
-          const T* vp = vt + voff + (16 * kc) * VSTR + 32 * nb;
-          const u32x2 lo = lds_read_tr16(vp);
-          const u32x2 hi = lds_read_tr16(vp + 8 * VSTR);
+          const u32x2 lo = lds_read_tr16(vt + 16 * kc * D + voff[0][nb]);
+          const u32x2 hi = lds_read_tr16(vt + 16 * kc * D + voff[1][nb]);
           const u32x4 cat = {lo[0], lo[1], hi[0], hi[1]};
           const v8 a = __builtin_bit_cast(v8, cat);
 #pragma unroll
@@ -270,8 +334,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
         }
     }
 
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+    // Tile j+1 has landed (this wave's share) and every LDS read of tile j
+    // has returned; after the barrier no wave reads tile j's buffer again, so
+    // the next step may start loading tile j+3 into it.
+    if (more) wait_counts<FWD_VMCNT_LGKM0(2 * SPW)>();
+    else wait_counts<FWD_VMCNT_LGKM0(0)>();
+    bare_barrier();
+  };
+  // Unrolled by three so each step names its ring buffers statically.
+  for (int j = 0; j < ntiles; j += 3) {
+    tile_step(j, K0, V0, K2, V2);
+    if (j + 1 < ntiles) tile_step(j + 1, K1, V1, K0, V0);
+    if (j + 2 < ntiles) tile_step(j + 2, K2, V2, K1, V1);
   }
 
   // Epilogue: O = O / l, lse = (m + log2 l) ln 2.
