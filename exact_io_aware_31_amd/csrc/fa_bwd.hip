@@ -113,8 +113,6 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
   constexpr int NB = D / 32;          // 32-column blocks of D
   constexpr int QB = BQ / 32;         // 32-row blocks of a query step
   constexpr int NDQ = NB * QB;        // 32x32 dQ output blocks per step
-  constexpr int CH = BQ * D / 8;      // 16-byte chunks per Q (or dO) tile
-  constexpr int CPT = (CH + BWD_THREADS - 1) / BWD_THREADS;
   __shared__ __attribute__((aligned(16))) T Qs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) T dOs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) T dSt[2][BK * BQ];  // dS^T: [key][query]
@@ -127,7 +125,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
   const int w = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
   const int bh = w / nkb;
   const int kblk = w % nkb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform_int(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int li = lane & 15, grp = lane >> 4;
   const size_t hoff = (size_t)bh * N * D;
@@ -192,18 +191,27 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
   const int trrow = 4 * hh + (li >> 2);
   const int trcol = 16 * (grp & 1) + 4 * (li & 3);
 
-  u32x4 qpre[CPT], dpre[CPT];
+  // Q and dO tiles of a query step go straight from global memory into LDS
+  // buffer `buf` (global_load_lds_dwordx4, no staging registers): wave w
+  // fills 1 KiB segments w SPW .. w SPW + SPW - 1 of each tile, lane l of
+  // segment g the LDS chunk slot l, i.e. tile row g RPS + l / (D / 8),
+  // physical chunk l mod (D / 8), with the logical chunk the swizzle puts
+  // there.  Rows past the end are clamped to row N-1 (their probabilities
+  // are masked to 0).  L and D for the step's rows go through registers.
+  constexpr int RPS = 512 / D;              // tile rows per 1 KiB segment
+  constexpr int NSEG = BQ * D * 2 / 1024;   // segments per Q (or dO) tile
+  constexpr int SPW = NSEG / 4;             // segments each wave loads
+  static_assert(NSEG % 4 == 0 && BWD_THREADS == 256, "tile segments split evenly over the waves");
   float lpre = 0.f, dpre_row = 0.f;
-  auto load_step = [&](int qi0) {
+  auto load_step = [&](int qi0, int buf) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int e = tid + i * BWD_THREADS;
-      if (CH % BWD_THREADS == 0 || e < CH) {
-        const int row = min(qi0 + e / (D / 8), N - 1), c8 = e % (D / 8);
-        const size_t off = (size_t)row * D + 8 * c8;
-        qpre[i] = *reinterpret_cast<const u32x4*>(Qh + off);
-        dpre[i] = *reinterpret_cast<const u32x4*>(dOh + off);
-      }
+    for (int i = 0; i < SPW; ++i) {
+      const int g = wave * SPW + i;
+      const int row = g * RPS + lane / (D / 8);
+      const int chunk = (lane % (D / 8)) ^ swz<D>(row);
+      const size_t off = (size_t)min(qi0 + row, N - 1) * D + 8 * chunk;
+      lds_load16(Qh + off, &Qs[buf][g * 512]);
+      lds_load16(dOh + off, &dOs[buf][g * 512]);
     }
     if (tid < BQ) {
       const int qrow = qi0 + tid;
@@ -212,15 +220,6 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
     }
   };
   auto store_step = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int e = tid + i * BWD_THREADS;
-      if (CH % BWD_THREADS == 0 || e < CH) {
-        const int row = e / (D / 8), col = 8 * (e % (D / 8));
-        *reinterpret_cast<u32x4*>(&Qs[buf][sw_off<D>(row, col)]) = qpre[i];
-        *reinterpret_cast<u32x4*>(&dOs[buf][sw_off<D>(row, col)]) = dpre[i];
-      }
-    }
     if (tid < BQ) {
       Ls2[buf][tid] = lpre;
       Dsh[buf][tid] = dpre_row;
@@ -267,8 +266,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
 
   const int qstart = CAUSAL ? kj0 : 0;
   const int nsteps = (N - qstart + BQ - 1) / BQ;
-  load_step(qstart);
+  load_step(qstart, 0);
   store_step(0);
+  wait_counts<FA_VMCNT_LGKM0(0)>();  // this wave's direct loads have landed
   __syncthreads();
 
   for (int it = 0; it < nsteps; ++it) {
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
     // The previous block's dQ first: its atomics then drain while this block
     // is computed (the wait for the prefetched tile below also covers them).
     if (it > 0) dq_step(buf ^ 1, qi0 - BQ);
-    if (it + 1 < nsteps) load_step(qi0 + BQ);
+    if (it + 1 < nsteps) load_step(qi0 + BQ, buf ^ 1);  // buffer the previous step read
 
     const T* __restrict__ qt = Qs[buf];
     const T* __restrict__ dt = dOs[buf];
@@ -380,6 +380,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_main_kernel(
     }
 
     if (it + 1 < nsteps) store_step(buf ^ 1);
+    wait_counts<FA_VMCNT_LGKM0(0)>();  // this wave's direct loads have landed
     __syncthreads();
   }
   if (nsteps > 0) dq_step((nsteps - 1) & 1, qstart + (nsteps - 1) * BQ);

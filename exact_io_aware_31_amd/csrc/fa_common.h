@@ -53,6 +53,37 @@ __device__ __forceinline__ void st16(void* p, V v) {
   *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+#define FA_VMCNT(n) ((((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14)))
+// ... and additionally until every LDS operation of this wave has completed.
+#define FA_VMCNT_LGKM0(n) (FA_VMCNT(n) & ~(15 << 8))
+
+// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base must be wave-uniform).
+__device__ __forceinline__ void lds_load16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+// Wait on this wave's outstanding counters.  The empty asm statements with a
+// memory clobber keep the compiler from moving LDS accesses across the wait
+// (the builtin alone is not a memory barrier to the compiler).
+template <int IMM>
+__device__ __forceinline__ void wait_counts() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(IMM);
+  asm volatile("" ::: "memory");
+}
+// Workgroup barrier without the memory fence of __syncthreads() (the fence
+// waits for every outstanding memory operation of the wave, including loads
+// issued for later tiles); the memory clobbers keep every LDS access on its
+// side of the barrier.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Round 8 floats to the storage type (round to nearest even).
 template <typename T>
 __device__ __forceinline__ typename Vec<T>::v8 to_v8(const float* x) {

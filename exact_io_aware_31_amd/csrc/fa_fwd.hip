@@ -58,11 +58,6 @@ constexpr int FWD_BR = FWD_NW * 32 * FWD_QG;
 constexpr int FWD_BC = 64;
 constexpr float FWD_RESCALE_SLACK = 8.0f;  // log2 units
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
-#define FWD_VMCNT(n) ((((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14)))
-// ... and additionally until every LDS operation of this wave has completed.
-#define FWD_VMCNT_LGKM0(n) (FWD_VMCNT(n) & ~(15 << 8))
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -75,29 +70,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16 l (lds_base must be wave-uniform).
-__device__ __forceinline__ void lds_load16(const void* gptr, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-// Wait on this wave's outstanding counters.  The empty asm statements with a
-// memory clobber keep the compiler from moving LDS accesses across the wait
-// (the builtin alone is not a memory barrier to the compiler).
-template <int IMM>
-__device__ __forceinline__ void wait_counts() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(IMM);
-  asm volatile("" ::: "memory");
-}
-// Workgroup barrier without the memory fence of __syncthreads() (which would
-// also wait for the loads of the tile after next); the memory clobbers keep
-// every LDS access on its side of the barrier.
-__device__ __forceinline__ void bare_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Chunk swizzle of tile row r (rows of D two-byte elements): 256-byte rows
 // use sw(r) = 4 (r mod 4) + (r / 4 mod 4), 128-byte rows sw(r) = r / 2 mod 8.
@@ -211,9 +183,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   if (ntiles > 1) {
     load_tile(Kh, K1, BC);
     load_tile(Vh, V1, BC);
-    wait_counts<FWD_VMCNT_LGKM0(2 * SPW)>();
+    wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
   } else {
-    wait_counts<FWD_VMCNT_LGKM0(0)>();
+    wait_counts<FA_VMCNT_LGKM0(0)>();
   }
   // A bare barrier: the waits above already cover what it must publish (a
   // fenced barrier would also wait for the loads of the tile after next).
@@ -337,8 +309,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     // Tile j+1 has landed (this wave's share) and every LDS read of tile j
     // has returned; after the barrier no wave reads tile j's buffer again, so
     // the next step may start loading tile j+3 into it.
-    if (more) wait_counts<FWD_VMCNT_LGKM0(2 * SPW)>();
-    else wait_counts<FWD_VMCNT_LGKM0(0)>();
+    if (more) wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
+    else wait_counts<FA_VMCNT_LGKM0(0)>();
     bare_barrier();
   };
   // Unrolled by three so each step names its ring buffers statically.
