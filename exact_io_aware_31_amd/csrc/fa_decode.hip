@@ -30,12 +30,30 @@ __device__ __forceinline__ void widen8(const typename Vec<T>::v8& x, float* f) {
   for (int i = 0; i < 8; ++i) f[i] = (float)x[i];
 }
 
-// Sum over the `width` consecutive lanes that share a key row (width = 8 or 16).
+// x + (x of the lane chosen by the DPP pattern), all in registers.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// Sum over the WIDTH consecutive lanes (8 or 16, aligned) that share a key
+// row, with DPP lane moves instead of LDS permutes: swap neighbours and
+// pairs inside each quad (quad_perm 1,0,3,2 and 2,3,0,1), then mirror within
+// each 8-lane half-row (every lane now holds its 8-lane sum) and, for 16,
+// within the 16-lane row.
 template <int WIDTH>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-  for (int off = WIDTH / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, WIDTH);
+  static_assert(WIDTH == 8 || WIDTH == 16, "8- or 16-lane rows");
+  x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_add<0x141>(x);  // row_half_mirror
+  if (WIDTH == 16) x = dpp_add<0x140>(x);  // row_mirror
   return x;
+}
+
+// Streaming 16-byte load (each K/V byte is read exactly once).
+template <typename V>
+__device__ __forceinline__ V ld16_stream(const void* p) {
+  return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -90,11 +108,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
     const int s1 = min(k_hi, s0 + DEC_SUB);
     // K pass: scores of keys s0..s1-1 into LDS.
     for (int kk = s0 + slot; kk < s1; kk += KPI * DEC_UNROLL) {
+      // Rows past the sub-chunk are clamped to its last row (always valid);
+      // their scores are never stored.
       v8 kr[DEC_UNROLL];
 #pragma unroll
       for (int u = 0; u < DEC_UNROLL; ++u) {
-        const int key = kk + u * KPI;
-        kr[u] = (key < s1) ? ld16<v8>(Kh + (size_t)key * D + 8 * col) : v8{};
+        const int key = min(kk + u * KPI, s1 - 1);
+        kr[u] = ld16_stream<v8>(Kh + (size_t)key * D + 8 * col);
       }
 #pragma unroll
       for (int u = 0; u < DEC_UNROLL; ++u) {
@@ -140,11 +160,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
     for (int i = 0; i < 8; ++i) o[i] *= alpha;
     // V pass: o += p * v over this lane's key rows.
     for (int kk = s0 + slot; kk < s1; kk += KPI * DEC_UNROLL) {
+      // Clamped rows as in the K pass; they get weight 0 below.
       v8 vr[DEC_UNROLL];
 #pragma unroll
       for (int u = 0; u < DEC_UNROLL; ++u) {
-        const int key = kk + u * KPI;
-        vr[u] = (key < s1) ? ld16<v8>(Vh + (size_t)key * D + 8 * col) : v8{};
+        const int key = min(kk + u * KPI, s1 - 1);
+        vr[u] = ld16_stream<v8>(Vh + (size_t)key * D + 8 * col);
       }
 #pragma unroll
       for (int u = 0; u < DEC_UNROLL; ++u) {
