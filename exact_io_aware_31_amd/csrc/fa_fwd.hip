@@ -233,6 +233,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
           for (int g = 0; g < QG; ++g)
             if (active[g]) sacc[g][sb] = mfma32x32x16(ka[kk & 1][sb], qf[g][kk], sacc[g][sb]);
       }
+      // Issue order of the score block: the K row reads run six reads (three
+      // MFMA pairs) ahead of the MFMAs that use them, instead of the
+      // scheduler's read-wait-use pairs.
+      {
+        constexpr int NM = (D / 16) * (BC / 32), PF = 6;
+        __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+        for (int i = 0; i < (NM - PF) / 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+      }
 
       v8 pb[QG][BC / 16];
 #pragma unroll
