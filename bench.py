@@ -33,12 +33,18 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 CSRC = os.path.join(ROOT, "exact_io_aware_31_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "bwd": "fa_bwd.hip", "decode": "fa_decode.hip"}
+# Each entry point's kernel source and the device headers it includes.
+KERNEL_SOURCES = {"fwd": ("fa_fwd.hip", "fa_tile.h", "fa_common.h"),
+                  "bwd": ("fa_bwd.hip", "fa_tile.h", "fa_common.h"),
+                  "decode": ("fa_decode.hip", "fa_common.h")}
 
 
 def source_sha(entry: str) -> str:
-    with open(os.path.join(CSRC, KERNEL_SOURCES[entry]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[entry]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(entry: str):

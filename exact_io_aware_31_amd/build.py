@@ -3,11 +3,10 @@
     python -m exact_io_aware_31_amd.build      # or build_library() from Python
 
 Every source is compiled for gfx950 only.  All HIP code is compiled with
-packed-fp32 instruction selection disabled (``-packed-fp32-ops``), with
-hardware float atomics enabled (``-munsafe-fp-atomics``, used by the backward
-pass's fp32 dQ accumulation) and with ``-fno-honor-nans``: the library's
-contract requires finite inputs, which lets max reductions compile to bare
-v_max/v_max3 without NaN-quieting canonicalisations.
+packed-fp32 instruction selection disabled (``-packed-fp32-ops``) and with
+``-fno-honor-nans``: the library's contract requires finite inputs, which
+lets max reductions compile to bare v_max/v_max3 without NaN-quieting
+canonicalisations.
 Output: exact_io_aware_31_amd/_lib/libfa.so.
 """
 import concurrent.futures as cf
@@ -36,7 +35,7 @@ def hipcc() -> str:
 def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-munsafe-fp-atomics", "-fno-honor-nans"]
+            "-fno-honor-nans"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -52,7 +52,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
-  return fa::bwd_dq_acc_bytes(B, H, N, d) + fa::bwd_drow_bytes(B, H, N);
+  return fa::bwd_drow_bytes(B, H, N);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -67,12 +67,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4) || !aligned(workspace, 16))
     return FA_ERR_ALIGN;
-  float* ws = static_cast<float*>(workspace);
-  float* dq_acc = ws;
-  float* drow = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         fa::bwd_dq_acc_bytes(B, H, N, d));
-  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, dq_acc, drow, B, H, N, d, scale, causal != 0,
-                to_dt(dt)};
+  float* drow = static_cast<float*>(workspace);
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, drow, B, H, N, d, scale, causal != 0, to_dt(dt)};
   return fa::launch_bwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -40,8 +40,8 @@
 //   * Grid: consecutive work items of one head are placed on one XCD (the
 //     hardware deals workgroups round-robin over the 8 XCDs) so the head's
 //     K/V stay in that XCD's L2; causal query blocks run heaviest first.
-#include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_tile.h"
 
 #ifndef FA_FWD_NW
 #define FA_FWD_NW 8
@@ -59,34 +59,6 @@ constexpr int FWD_BC = 64;
 constexpr float FWD_RESCALE_SLACK = 8.0f;  // log2 units
 
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
-// (i mod 4) of the 4-element rows addressed by lanes i/4, 4 + i/4, 8 + i/4
-// and 12 + i/4 of its group.
-__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-
-// Chunk swizzle of tile row r (rows of D two-byte elements): 256-byte rows
-// use sw(r) = 4 (r mod 4) + (r / 4 mod 4), 128-byte rows sw(r) = r / 2 mod 8.
-// Either way sixteen consecutive rows read at one logical chunk touch every
-// bank once, and the 4-row x 32-byte footprint of a transpose read is
-// conflict-free.  The swizzle depends on r mod 16 only.
-template <int D>
-__device__ __forceinline__ int fwd_swz(int r) {
-  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
-}
-// Element offset of (row, col) in a swizzled tile.
-template <int D>
-__device__ __forceinline__ int fwd_toff(int row, int col) {
-  return row * D + ((((col >> 3) ^ fwd_swz<D>(row)) << 3) | (col & 7));
-}
-
 template <typename T, int D, bool CAUSAL, int NW, int QG>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -95,10 +67,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   using v4 = typename Vec<T>::v4;
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32 * QG, BC = FWD_BC;
-  constexpr int RPS = 512 / D;                  // tile rows per 1 KiB load segment
-  constexpr int NSEG = BC * D * 2 / 1024;       // segments per tile
-  constexpr int SPW = NSEG / NW;                // segments each wave loads
-  static_assert(NSEG % NW == 0 && NT == 512, "tile segments split evenly over the waves");
+  constexpr int SPW = BC * D * 2 / 1024 / NW;  // tile load segments per wave (vmcnt units)
+  static_assert(NT == 512, "two waves per SIMD at one workgroup per CU");
   // Three-deep ring of K and V tiles (separate arrays, so every access names
   // its buffer statically and the compiler sees which loads it depends on).
   __shared__ __attribute__((aligned(1024))) T K0[BC * D], K1[BC * D], K2[BC * D];
@@ -144,21 +114,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   const int kv_end = CAUSAL ? min(N, (qb + 1) * BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  // Tile loads: wave w fills segments w SPW .. w SPW + SPW - 1 of a tile; lane
-  // l of segment g fills LDS chunk slot l of the segment, i.e. tile row
-  // g RPS + l / (D / 8), physical chunk l mod (D / 8), with the logical chunk
-  // that the swizzle puts there.  Rows past the end are clamped to row N-1:
+  // Tile loads (see load_tile): rows past the end are clamped to row N-1;
   // those keys are masked to -inf before the softmax, so their probabilities
   // (and their V rows' weight) are 0.
-  auto load_tile = [&](const T* __restrict__ src, T* dst, int kb) {
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-      const int g = wave * SPW + i;
-      const int row = g * RPS + lane / (D / 8);
-      const int chunk = (lane % (D / 8)) ^ fwd_swz<D>(row);
-      const T* gp = src + (size_t)min(kb + row, N - 1) * D + 8 * chunk;
-      lds_load16(gp, dst + g * 512);
-    }
+  auto load_kv = [&](const T* __restrict__ src, T* dst, int kb) {
+    load_tile<T, D, BC, NW>(src, dst, kb, N, wave, lane);
   };
   // Per-lane element offsets of the operand reads (the swizzle depends on the
   // row mod 16 only, so they hold for every 16- or 32-row block of a tile):
@@ -168,21 +128,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   //    + 4 (i mod 4).
   int koff[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = fwd_toff<D>(l32, 16 * kk + 8 * hh);
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off<D>(l32, 16 * kk + 8 * hh);
   const int grp = lane >> 4, li = lane & 15;
   int voff[2][D / 32];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb)
-      voff[t][nb] = fwd_toff<D>(8 * t + 4 * hh + (li >> 2), 32 * nb + 16 * (grp & 1) + 4 * (li & 3));
+      voff[t][nb] = tile_off<D>(8 * t + 4 * hh + (li >> 2), 32 * nb + 16 * (grp & 1) + 4 * (li & 3));
 
   // Tiles 0 and 1 in flight; wait for tile 0 (vmcnt counts this wave's loads).
-  load_tile(Kh, K0, 0);
-  load_tile(Vh, V0, 0);
+  load_kv(Kh, K0, 0);
+  load_kv(Vh, V0, 0);
   if (ntiles > 1) {
-    load_tile(Kh, K1, BC);
-    load_tile(Vh, V1, BC);
+    load_kv(Kh, K1, BC);
+    load_kv(Vh, V1, BC);
     wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
   } else {
     wait_counts<FA_VMCNT_LGKM0(0)>();
@@ -197,8 +157,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     const int kb = j * BC;
     const bool more = j + 2 < ntiles;
     if (more) {
-      load_tile(Kh, kn, kb + 2 * BC);
-      load_tile(Vh, vn, kb + 2 * BC);
+      load_kv(Kh, kn, kb + 2 * BC);
+      load_kv(Vh, vn, kb + 2 * BC);
     }
     bool active[QG];
     bool any_active = false;

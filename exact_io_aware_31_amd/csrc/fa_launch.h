@@ -22,7 +22,6 @@ struct BwdArgs {
   const void* q; const void* k; const void* v; const void* o;
   const float* lse; const void* dout;
   void* dq; void* dk; void* dv;
-  float* dq_acc;   // [B,H,N,d] float32 workspace
   float* drow;     // [B,H,N] float32 workspace
   int B, H, N, d;
   float scale;
@@ -45,7 +44,6 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 // Workspace layouts (bytes), shared by the size queries and the launchers.
-size_t bwd_dq_acc_bytes(int B, int H, int N, int d);
 size_t bwd_drow_bytes(int B, int H, int N);
 size_t decode_part_o_bytes(int B, int H, int d, int splits);
 size_t decode_part_lse_bytes(int B, int H, int splits);

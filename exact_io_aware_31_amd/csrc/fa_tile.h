@@ -1,0 +1,66 @@
+// fa_tile.h -- key / value tiles in LDS for the kernels that stream blocks of
+// keys past a resident block of query rows (the forward pass and the dQ pass
+// of the backward).
+//
+// A tile holds BC consecutive rows of a [N, D] head (D two-byte elements per
+// row), unpadded, with 16-byte chunk c of row r stored at chunk c ^ sw(r).
+// 256-byte rows use sw(r) = 4 (r mod 4) + (r / 4 mod 4), 128-byte rows
+// sw(r) = r / 2 mod 8.  Either way sixteen consecutive rows read at one
+// logical chunk touch every bank once, and the 4-row x 32-byte footprint of a
+// transpose read is conflict-free.  The swizzle depends on r mod 16 only, so
+// per-lane offsets computed for rows 0..15 (or 0..31) hold for every 16-row
+// (32-row) block of a tile.
+#pragma once
+
+#include "fa_common.h"
+
+namespace fa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i mod 4) of the 4-element rows addressed by lanes i/4, 4 + i/4, 8 + i/4
+// and 12 + i/4 of its group.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+template <int D>
+struct TileSwizzle {
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  static __device__ __forceinline__ int sw(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
+  }
+};
+// Element offset of (row, col) in a tile of rows of D elements swizzled by SW.
+template <int D, typename SW = TileSwizzle<D>>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ SW::sw(row)) << 3) | (col & 7));
+}
+
+// Direct global-to-LDS load of rows kb .. kb + BC - 1 of a head into the tile
+// at dst by NW waves: the tile is cut into 1 KiB segments, wave w fills
+// segments w SPW .. w SPW + SPW - 1, and lane l of segment g fills LDS chunk
+// slot l of it, i.e. tile row g RPS + l / (D / 8), physical chunk
+// l mod (D / 8), with the logical chunk the swizzle puts there.  Rows past
+// the end are clamped to row N-1 (callers mask those rows).  Each wave issues
+// SPW loads, counted by its vmcnt.  SW is the tile's chunk swizzle.
+template <typename T, int D, int BC, int NW, typename SW = TileSwizzle<D>>
+__device__ __forceinline__ void load_tile(const T* __restrict__ src, T* dst, int kb, int N,
+                                          int wave, int lane) {
+  constexpr int RPS = 512 / D;             // tile rows per 1 KiB segment
+  constexpr int NSEG = BC * D * 2 / 1024;  // segments per tile
+  constexpr int SPW = NSEG / NW;           // segments each wave loads
+  static_assert(NSEG % NW == 0, "tile segments split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int g = wave * SPW + i;
+    const int row = g * RPS + lane / (D / 8);
+    const int chunk = (lane % (D / 8)) ^ SW::sw(row);
+    lds_load16(src + (size_t)min(kb + row, N - 1) * D + 8 * chunk, dst + g * 512);
+  }
+}
+
+}  // namespace fa

@@ -81,8 +81,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int N, int d, float scale, int causal, fa_dtype dt,
                  void* stream);
 
-/* Bytes of device workspace fa_bwd needs: a float32 dQ accumulator
- * [B, H, N, d] and the float32 row terms D [B, H, N], 256-byte aligned. */
+/* Bytes of device workspace fa_bwd needs: the float32 row terms
+ * D_i = sum_k dout_ik o_ik, [B, H, N], rounded up to 256 bytes (d is only
+ * checked). */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
@@ -95,8 +96,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   dq, dk, dv      out: [B, H, N, d], dt
  *   workspace           : device scratch of at least fa_bwd_workspace_bytes;
  *                         contents on entry are ignored, on exit undefined.
- * dq is accumulated with float32 atomics, so its low bits may differ between
- * runs; dk and dv are deterministic.
+ * Every output element is written once, without atomics: results are
+ * deterministic (bitwise equal across runs with the same inputs).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -49,9 +49,10 @@ def test_status_strings_and_version(lib):
 
 
 def test_workspace_sizes(lib):
-    # fp32 dQ accumulator + fp32 row terms, each rounded up to 256 bytes
-    assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 128 * 4 + 2 * 16 * 4096 * 4
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 768 + 256
+    # fp32 row terms D, rounded up to 256 bytes
+    assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256
+    assert fa.fa_bwd_workspace_bytes(1, 1, 65, 128) == 512
     # fp32 partial outputs + fp32 partial lse
     assert fa.fa_decode_workspace_bytes(64, 32, 128, 16) == 64 * 32 * 16 * 128 * 4 + 64 * 32 * 16 * 4
     assert fa.fa_decode_workspace_bytes(1, 1, 64, 3) == 768 + 256

@@ -63,9 +63,9 @@ def test_bwd_full_size_workload():
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_bwd_wide_key_blocks(causal, d, dtype):
-    """Enough heads that the launcher picks 256 keys per workgroup (B H ceil(N/256) >= 1024);
-    N = 500 leaves a ragged last key block."""
+def test_bwd_many_heads(causal, d, dtype):
+    """A grid of several workgroups per CU in both passes (512 heads); N = 500 leaves a ragged
+    last key block (dK/dV pass) and a ragged last query block (dQ pass)."""
     B, H, N = 2, 256, 500
     seed = 8500 + d + (1 if causal else 0)
     announce(f"bwd wide blocks B{B} H{H} N{N} d{d} causal={causal} {dtype} seed={seed}")
@@ -89,3 +89,19 @@ def test_bwd_at_bench_shape():
         ref = oracle.attn_bwd(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
         for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
             check_rel_norm(host64(g[b, h]), r, w.dtype, f"{name} head ({b},{h})")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bwd_deterministic(causal):
+    """Every gradient element is written once by one lane (no atomics): repeated calls on the
+    same inputs give bitwise-equal dQ, dK and dV."""
+    B, H, N, d, dtype = 2, 8, 1000, 128, torch.bfloat16
+    seed = 8700 + (1 if causal else 0)
+    announce(f"bwd determinism B{B} H{H} N{N} d{d} causal={causal} seed={seed}")
+    q, k, v, do = attention_inputs(B, H, N, d, dtype, seed, DEV, with_dout=True)
+    scale = d ** -0.5
+    first = run_fwd_bwd(q, k, v, do, scale, causal)
+    for _ in range(2):
+        again = run_fwd_bwd(q, k, v, do, scale, causal)
+        for name, a, b in zip(("dQ", "dK", "dV"), first, again):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name} differs between runs"
