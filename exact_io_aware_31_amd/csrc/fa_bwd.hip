@@ -36,10 +36,9 @@
 // must either sum dQ over key blocks with atomics or sum dK, dV over query
 // blocks the same way; the extra matrix work costs less than either.
 //
-// LDS tiles are unpadded, with 16-byte chunk c of row r stored at chunk
-// c ^ sw(r), and are filled by direct global-to-LDS loads.  The dQ pass uses
-// the forward's swizzle; the dK/dV pass, which is short of registers, a
-// 3-bit one that leaves chunk bit 3 alone (see KvSwizzle).
+// LDS tiles use the forward's unpadded, swizzled layout (fa_tile.h: 16-byte
+// row reads and transpose reads conflict-free) and are filled by direct
+// global-to-LDS loads.
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -68,17 +67,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 }
 
 // ---------------------------------------------------------------- kernel 2
-// Swizzle of the dK/dV pass's tiles: sw(r) = 2 (r mod 4) + (r / 4 mod 2).
-// Eight consecutive rows hit eight different chunks, so 16-byte row reads
-// take at most two passes, and four consecutive rows hit four different chunk
-// pairs, so transpose reads are conflict-free.  As chunk bit 3 is never
-// flipped, a lane's row reads need only four base offsets (chunks 8 and up
-// are 64 elements further), and rows r and r + 8 share a swizzle.
-template <int D>
-struct KvSwizzle {
-  static __device__ __forceinline__ int sw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-};
-
 constexpr int KV_WAVES = 4;
 constexpr int KV_BK = 32 * KV_WAVES;  // keys per workgroup
 constexpr int KV_BQ = 32;             // query rows per step
@@ -126,35 +114,39 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   for (int kk = 0; kk < D / 16; ++kk)
     vf[kk] = key_ok ? ld16<v8>(Vh + (size_t)mykey * D + 16 * kk + 8 * hh) : v8{};
   // Rows past the end are clamped to row N-1; those keys' scores are masked.
-  load_tile<T, D, BK, KV_WAVES, KvSwizzle<D>>(Kh, Ks, kj0, N, wave, lane);
+  load_tile<T, D, BK, KV_WAVES>(Kh, Ks, kj0, N, wave, lane);
 
   f32x16 dvacc[NB], dkacc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) { dvacc[i] = f32x16{}; dkacc[i] = f32x16{}; }
 
-  // Per-lane element offsets (the swizzle depends on the row mod 8):
-  //  * 16-byte row reads (A operands Q and dO of S and dP, B operand K_w of
-  //    S): row l32, columns 16 kk + 8 hh, at rowoff[kk mod 4] + 64 (kk / 4).
-  //  * transpose reads (B operands of dK / dV from the Q / dO tiles): lane li
-  //    of 16-lane group grp addresses row 16 kc + 8 t + 4 hh + li / 4, column
-  //    32 nb + 16 (grp mod 2) + 4 (li mod 4); the reduction index (query)
-  //    comes out in the order the 32x32 accumulator layout hands P and dS to
-  //    the A operand.
-  using SW = KvSwizzle<D>;
-  int rowoff[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) rowoff[m] = tile_off<D, SW>(l32, 16 * m + 8 * hh);
-  auto roff = [&](int kk) { return rowoff[kk & 3] + 64 * (kk >> 2); };
-  const int trrow = 4 * hh + (li >> 2);
-  const int trcol = 16 * (grp & 1) + 4 * (li & 3);
+  // LDS byte offsets.  The swizzle only XORs chunk bits, so a lane's 16-byte
+  // row reads (row l32, columns 16 kk + 8 hh: A operands Q and dO of S and dP,
+  // B operand K_w of S) sit at rb ^ 32 kk, and its transpose reads (B
+  // operands of dK / dV from the Q / dO tiles: row 16 kc + 8 t + 4 hh + li / 4,
+  // column 32 nb + 16 (grp mod 2) + 4 (li mod 4)) at (tb ^ trx(t, nb)) +
+  // 32 D kc, with trx the offset of (row 8 t, column 32 nb).  Three base
+  // registers and one XOR per read replace a table of sixteen offsets, which
+  // this kernel has no registers for.  The transpose reads hand the reduction
+  // index (query) over in the order the 32x32 accumulator layout gives P and
+  // dS to the A operand.
+  const uint32_t rb = 2 * tile_off<D>(l32, 8 * hh);
+  const uint32_t tb = 2 * tile_off<D>(4 * hh + (li >> 2), 16 * (grp & 1) + 4 * (li & 3));
+  const uint32_t kwb = rb + 64 * D * wave;  // this wave's 32 K rows (a multiple of the tile size apart)
+  auto row_read = [](const T* tile, uint32_t off) {
+    return *reinterpret_cast<const v8*>(reinterpret_cast<const char*>(tile) + off);
+  };
+  auto tr_read = [](const T* tile, uint32_t off) {
+    return lds_read_tr16(reinterpret_cast<const char*>(tile) + off);
+  };
 
   // Q and dO tiles of a step go straight into LDS buffer `buf` (rows past the
   // end clamped to row N-1, their probabilities masked to 0); L and D of the
   // step's rows go through registers.
   float lpre = 0.f, dpre = 0.f;
   auto load_step = [&](int qi0, int buf) {
-    load_tile<T, D, BQ, KV_WAVES, SW>(Qh, Qs[buf], qi0, N, wave, lane);
-    load_tile<T, D, BQ, KV_WAVES, SW>(dOh, dOs[buf], qi0, N, wave, lane);
+    load_tile<T, D, BQ, KV_WAVES>(Qh, Qs[buf], qi0, N, wave, lane);
+    load_tile<T, D, BQ, KV_WAVES>(dOh, dOs[buf], qi0, N, wave, lane);
     if (tid < BQ) {
       const int qrow = qi0 + tid;
       lpre = (qrow < N) ? Lh[qrow] * 1.4426950408889634f : 0.f;
@@ -176,13 +168,16 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   wait_counts<FA_VMCNT_LGKM0(0)>();  // this wave's direct loads (K tile included) have landed
   __syncthreads();
 
-  const T* __restrict__ kw = Ks + 32 * wave * D;  // this wave's 32 key rows
   for (int it = 0; it < nsteps; ++it) {
     const int qi0 = qstart + it * BQ, buf = it & 1;
     if (it + 1 < nsteps) load_step(qi0 + BQ, buf ^ 1);  // buffer the previous step read
 
-    const T* __restrict__ qt = Qs[buf];
-    const T* __restrict__ dt = dOs[buf];
+    // This step's buffer: tiles are 32 D * 2 bytes apart, above every in-tile
+    // offset, so adding the buffer offset commutes with the XORs.  The empty
+    // asm makes the bases opaque, so the XORs stay in the loop rather than
+    // being hoisted into sixteen loop-invariant registers.
+    uint32_t rbs = rb + buf * (BQ * D * 2), tbs = tb + buf * (BQ * D * 2), kws = kwb;
+    asm volatile("" : "+v"(rbs), "+v"(tbs), "+v"(kws));
     // Let the scheduler interleave the LDS reads with the matrix products.
     __builtin_amdgcn_iglp_opt(0);
     // Visibility: query qi0 + ql sees key mykey iff ql >= mykey - qi0 (causal),
@@ -196,48 +191,49 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     f32x16 sa = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const v8 aq = *reinterpret_cast<const v8*>(&qt[roff(kk)]);
-      const v8 bk = *reinterpret_cast<const v8*>(&kw[roff(kk)]);
+      const v8 aq = row_read(Qs[0], rbs ^ (32 * kk));
+      const v8 bk = row_read(Ks, kws ^ (32 * kk));
       sa = mfma32x32x16(aq, bk, sa);
     }
+    // P = exp2(c S - L log2 e) for every element, then, on the few steps that
+    // need it (the wave's diagonal step and the ragged ends), the masked
+    // elements are zeroed.  The empty volatile asm keeps that a real branch:
+    // flattened into selects it would cost five instructions per score on
+    // every step.  Unmasked garbage never reaches a product.
+    float pv[16];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      float pv[8];
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][8 * g + 4 * hh]);
 #pragma unroll
-      for (int g2 = 0; g2 < 2; ++g2) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][16 * hf + 8 * g2 + 4 * hh]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * hf + 4 * g2 + e;
-          float pe = fast_exp2(__builtin_fmaf(sa[r], c, -l4[e]));
-          if (need_mask) {
-            const int qc = 8 * (r >> 2) + (r & 3);  // query offset minus 4 hh
-            pe = (qc >= lo && qc < hi) ? pe : 0.f;
-          }
-          pv[4 * g2 + e] = pe;
-        }
-      }
-      pA[hf] = to_v8<T>(pv);
+      for (int e = 0; e < 4; ++e) pv[4 * g + e] = fast_exp2(__builtin_fmaf(sa[4 * g + e], c, -l4[e]));
     }
+    if (need_mask) {
+      asm volatile("");
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qc = 8 * (r >> 2) + (r & 3);  // query offset minus 4 hh
+        pv[r] = (qc >= lo && qc < hi) ? pv[r] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) pA[hf] = to_v8<T>(&pv[8 * hf]);
     // dP = dO V_w^T, then dS = P o (dP - D) with P as rounded for the P^T dO
     // product (dS is rounded to the storage type as well).
     f32x16 dp = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const v8 ad = *reinterpret_cast<const v8*>(&dt[roff(kk)]);
+      const v8 ad = row_read(dOs[0], rbs ^ (32 * kk));
       dp = mfma32x32x16(ad, vf[kk], dp);
     }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      float dsv[8];
+      float pr[8], dsv[8];
+      from_v8(pA[hf], pr);
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][16 * hf + 8 * g2 + 4 * hh]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * hf + 4 * g2 + e;
-          dsv[4 * g2 + e] = (float)pA[hf][4 * g2 + e] * (dp[r] - d4[e]);
-        }
+        for (int e = 0; e < 4; ++e) dsv[4 * g2 + e] = pr[4 * g2 + e] * (dp[8 * hf + 4 * g2 + e] - d4[e]);
       }
       dsA[hf] = to_v8<T>(dsv);
     }
@@ -247,12 +243,12 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int kc = 0; kc < BQ / 16; ++kc) {
-        const int o0 = tile_off<D, SW>(16 * kc + trrow, 32 * nb + trcol);
-        const int o1 = o0 + 8 * D;  // row + 8: same swizzle
-        const u32x2 d0 = lds_read_tr16(&dt[o0]);
-        const u32x2 d1 = lds_read_tr16(&dt[o1]);
-        const u32x2 q0 = lds_read_tr16(&qt[o0]);
-        const u32x2 q1 = lds_read_tr16(&qt[o1]);
+        const uint32_t o0 = (tbs ^ (2 * tile_off<D>(0, 32 * nb))) + 32 * D * kc;
+        const uint32_t o1 = (tbs ^ (2 * tile_off<D>(8, 32 * nb))) + 32 * D * kc;
+        const u32x2 d0 = tr_read(dOs[0], o0);
+        const u32x2 d1 = tr_read(dOs[0], o1);
+        const u32x2 q0 = tr_read(Qs[0], o0);
+        const u32x2 q1 = tr_read(Qs[0], o1);
         const u32x4 cd = {d0[0], d0[1], d1[0], d1[1]};
         const u32x4 cq = {q0[0], q0[1], q1[0], q1[1]};
         dvacc[nb] = mfma32x32x16(pA[kc], __builtin_bit_cast(v8, cd), dvacc[nb]);

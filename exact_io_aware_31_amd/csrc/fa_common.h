@@ -93,4 +93,20 @@ __device__ __forceinline__ typename Vec<T>::v8 to_v8(const float* x) {
   return r;
 }
 
+// The 8 values of a packed vector as floats (exact).  For bfloat16 this is a
+// shift or a mask per value, done on the packed words so the compiler does not
+// round each value separately to recover it.
+__device__ __forceinline__ void from_v8(bf16x8 v, float* x) {
+  const u32x4 w = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void from_v8(f16x8 v, float* x) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+}
+
 }  // namespace fa
