@@ -120,25 +120,17 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
 #pragma unroll
   for (int i = 0; i < NB; ++i) { dvacc[i] = f32x16{}; dkacc[i] = f32x16{}; }
 
-  // LDS byte offsets.  The swizzle only XORs chunk bits, so a lane's 16-byte
-  // row reads (row l32, columns 16 kk + 8 hh: A operands Q and dO of S and dP,
-  // B operand K_w of S) sit at rb ^ 32 kk, and its transpose reads (B
-  // operands of dK / dV from the Q / dO tiles: row 16 kc + 8 t + 4 hh + li / 4,
-  // column 32 nb + 16 (grp mod 2) + 4 (li mod 4)) at (tb ^ trx(t, nb)) +
-  // 32 D kc, with trx the offset of (row 8 t, column 32 nb).  Three base
-  // registers and one XOR per read replace a table of sixteen offsets, which
-  // this kernel has no registers for.  The transpose reads hand the reduction
-  // index (query) over in the order the 32x32 accumulator layout gives P and
-  // dS to the A operand.
-  const uint32_t rb = 2 * tile_off<D>(l32, 8 * hh);
-  const uint32_t tb = 2 * tile_off<D>(4 * hh + (li >> 2), 16 * (grp & 1) + 4 * (li & 3));
-  const uint32_t kwb = rb + 64 * D * wave;  // this wave's 32 K rows (a multiple of the tile size apart)
-  auto row_read = [](const T* tile, uint32_t off) {
-    return *reinterpret_cast<const v8*>(reinterpret_cast<const char*>(tile) + off);
-  };
-  auto tr_read = [](const T* tile, uint32_t off) {
-    return lds_read_tr16(reinterpret_cast<const char*>(tile) + off);
-  };
+  // LDS byte offsets by XOR addressing (fa_tile.h): 16-byte row reads (row
+  // l32, columns 16 kk + 8 hh: A operands Q and dO of S and dP, B operand K_w
+  // of S) and transpose reads (B operands of dK / dV from the Q / dO tiles:
+  // row 16 kc + 8 t + 4 hh + li / 4, column 32 nb + 16 (grp mod 2) +
+  // 4 (li mod 4)).  Three base registers and one XOR per read replace a table
+  // of sixteen offsets, which this kernel has no registers for.  The
+  // transpose reads hand the reduction index (query) over in the order the
+  // 32x32 accumulator layout gives P and dS to the A operand.
+  const uint32_t rb = tile_row_base<D>(l32, hh);
+  const uint32_t tb = tile_tr_base<D>(4 * hh + (li >> 2), 16 * (grp & 1) + 4 * (li & 3));
+  const uint32_t kwb = rb + 64 * D * wave;  // this wave's 32 K rows: 32 D * 2 bytes per wave
 
   // Q and dO tiles of a step go straight into LDS buffer `buf` (rows past the
   // end clamped to row N-1, their probabilities masked to 0); L and D of the
@@ -186,20 +178,31 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     const int lo = CAUSAL ? mykey - qi0 - 4 * hh : -(1 << 30);
     const int hi = (key_ok ? N - qi0 : 0) - 4 * hh;
 
-    // S = Q K_w^T (keys on the lanes), then P (kept only in the storage type).
+    // Issue order within the step: both score-shaped products first (S =
+    // Q K_w^T and dP = dO V_w^T, keys on the lanes), so the exponentials of P
+    // run beside the dP MFMAs; then dV += P^T dO, beside which the dS
+    // arithmetic runs; then dK += dS^T Q.  Within one wave a few VALU
+    // instructions per MFMA are nearly free, so each VALU phase hides behind
+    // independent matrix work instead of stalling between two products.
     v8 pA[BQ / 16], dsA[BQ / 16];
-    f32x16 sa = f32x16{};
+    f32x16 sa = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const v8 aq = row_read(Qs[0], rbs ^ (32 * kk));
-      const v8 bk = row_read(Ks, kws ^ (32 * kk));
+      const v8 aq = lds_at<v8>(Qs[0], rbs ^ (32 * kk));
+      const v8 bk = lds_at<v8>(Ks, kws ^ (32 * kk));
       sa = mfma32x32x16(aq, bk, sa);
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const v8 ad = lds_at<v8>(dOs[0], rbs ^ (32 * kk));
+      dp = mfma32x32x16(ad, vf[kk], dp);
     }
     // P = exp2(c S - L log2 e) for every element, then, on the few steps that
     // need it (the wave's diagonal step and the ragged ends), the masked
     // elements are zeroed.  The empty volatile asm keeps that a real branch:
     // flattened into selects it would cost five instructions per score on
-    // every step.  Unmasked garbage never reaches a product.
+    // every step.  Unmasked garbage never reaches a product.  P is kept only
+    // in the storage type.
     float pv[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -217,14 +220,19 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) pA[hf] = to_v8<T>(&pv[8 * hf]);
-    // dP = dO V_w^T, then dS = P o (dP - D) with P as rounded for the P^T dO
-    // product (dS is rounded to the storage type as well).
-    f32x16 dp = f32x16{};
+
+    // dV_w += P^T dO_i; the B operand comes from transpose reads of the dO tile.
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const v8 ad = row_read(dOs[0], rbs ^ (32 * kk));
-      dp = mfma32x32x16(ad, vf[kk], dp);
-    }
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int kc = 0; kc < BQ / 16; ++kc) {
+        const u32x2 d0 = lds_tr_at(dOs[0], (tbs ^ tile_tr_xor<D>(0, nb)) + 32 * D * kc);
+        const u32x2 d1 = lds_tr_at(dOs[0], (tbs ^ tile_tr_xor<D>(1, nb)) + 32 * D * kc);
+        const u32x4 cd = {d0[0], d0[1], d1[0], d1[1]};
+        dvacc[nb] = mfma32x32x16(pA[kc], __builtin_bit_cast(v8, cd), dvacc[nb]);
+      }
+    // dS = P o (dP - D) with P as rounded for the P^T dO product (dS is
+    // rounded to the storage type as well).
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       float pr[8], dsv[8];
@@ -237,21 +245,14 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
       }
       dsA[hf] = to_v8<T>(dsv);
     }
-
-    // dV_w += P^T dO_i and dK_w += dS^T Q_i (scale applied at the end).
+    // dK_w += dS^T Q_i (scale applied at the end), Q^T by transpose reads.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int kc = 0; kc < BQ / 16; ++kc) {
-        const uint32_t o0 = (tbs ^ (2 * tile_off<D>(0, 32 * nb))) + 32 * D * kc;
-        const uint32_t o1 = (tbs ^ (2 * tile_off<D>(8, 32 * nb))) + 32 * D * kc;
-        const u32x2 d0 = tr_read(dOs[0], o0);
-        const u32x2 d1 = tr_read(dOs[0], o1);
-        const u32x2 q0 = tr_read(Qs[0], o0);
-        const u32x2 q1 = tr_read(Qs[0], o1);
-        const u32x4 cd = {d0[0], d0[1], d1[0], d1[1]};
+        const u32x2 q0 = lds_tr_at(Qs[0], (tbs ^ tile_tr_xor<D>(0, nb)) + 32 * D * kc);
+        const u32x2 q1 = lds_tr_at(Qs[0], (tbs ^ tile_tr_xor<D>(1, nb)) + 32 * D * kc);
         const u32x4 cq = {q0[0], q0[1], q1[0], q1[1]};
-        dvacc[nb] = mfma32x32x16(pA[kc], __builtin_bit_cast(v8, cd), dvacc[nb]);
         dkacc[nb] = mfma32x32x16(dsA[kc], __builtin_bit_cast(v8, cq), dkacc[nb]);
       }
 
@@ -329,19 +330,12 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
   auto load_kv = [&](const T* __restrict__ src, T* dst, int kb) {
     load_tile<T, D, BC, NW>(src, dst, kb, N, wave, lane);
   };
-  // Per-lane element offsets: K and V rows (A operands of S^T and dP^T) at
-  // row l32, columns 16 kk + 8 hh; K^T (A operand of dQ^T += K^T dS^T) by
-  // transpose reads, lane li of group grp at key 8 t + 4 hh + li / 4,
-  // columns 32 nb + 16 (grp mod 2) + 4 (li mod 4).
-  int koff[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off<D>(l32, 16 * kk + 8 * hh);
-  int troff[2][NB];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      troff[t][nb] = tile_off<D>(8 * t + 4 * hh + (li >> 2), 32 * nb + 16 * (grp & 1) + 4 * (li & 3));
+  // LDS byte offsets by XOR addressing (fa_tile.h): K and V rows (A operands
+  // of S^T and dP^T) at row l32, columns 16 kk + 8 hh; K^T (A operand of
+  // dQ^T += K^T dS^T) by transpose reads, lane li of group grp at key
+  // 8 t + 4 hh + li / 4, columns 32 nb + 16 (grp mod 2) + 4 (li mod 4).
+  const uint32_t rb = tile_row_base<D>(l32, hh);
+  const uint32_t tb = tile_tr_base<D>(4 * hh + (li >> 2), 16 * (grp & 1) + 4 * (li & 3));
 
   // Tiles 0 and 1 in flight; wait for tile 0.
   load_kv(Kh, K0, 0);
@@ -372,14 +366,18 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
       int lim = N - 1 - kb;
       if (CAUSAL) lim = min(lim, myq - kb);
       lim -= 4 * hh;
+      // Opaque copies of the bases keep the XORs per tile instead of hoisted
+      // into sixteen loop-invariant registers.
+      uint32_t rbs = rb, tbs = tb;
+      asm volatile("" : "+v"(rbs), "+v"(tbs));
       v8 dsb[BC / 16];
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const v8 ak = *reinterpret_cast<const v8*>(kt + 32 * sb * D + koff[kk]);
-          const v8 av = *reinterpret_cast<const v8*>(vt + 32 * sb * D + koff[kk]);
+          const v8 ak = lds_at<v8>(kt, (rbs ^ (32 * kk)) + 64 * D * sb);
+          const v8 av = lds_at<v8>(vt, (rbs ^ (32 * kk)) + 64 * D * sb);
           s = mfma32x32x16(ak, qf[kk], s);
           dp = mfma32x32x16(av, dof[kk], dp);
         }
@@ -404,8 +402,8 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int kc = 0; kc < BC / 16; ++kc) {
-          const u32x2 lo = lds_read_tr16(kt + 16 * kc * D + troff[0][nb]);
-          const u32x2 hi = lds_read_tr16(kt + 16 * kc * D + troff[1][nb]);
+          const u32x2 lo = lds_tr_at(kt, (tbs ^ tile_tr_xor<D>(0, nb)) + 32 * D * kc);
+          const u32x2 hi = lds_tr_at(kt, (tbs ^ tile_tr_xor<D>(1, nb)) + 32 * D * kc);
           const u32x4 cat = {lo[0], lo[1], hi[0], hi[1]};
           dqacc[nb] = mfma32x32x16(__builtin_bit_cast(v8, cat), dsb[kc], dqacc[nb]);
         }

@@ -40,6 +40,31 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * D + ((((col >> 3) ^ SW::sw(row)) << 3) | (col & 7));
 }
 
+// XOR addressing.  The swizzle only XORs chunk bits, so the byte offsets of
+// a lane's reads are one base XOR a compile-time constant:
+//   * 16-byte row read of row r, columns 16 kk + 8 h:
+//       tile_row_base<D>(r, h) ^ (32 kk);
+//   * transpose read of row 16 kc + 8 t + r0, columns 32 nb + c0 (r0 < 8,
+//     c0 < 32, c0 a multiple of 4):
+//       (tile_tr_base<D>(r0, c0) ^ tile_tr_xor<D>(t, nb)) + 32 D kc.
+// A kernel short of registers keeps the two bases instead of a table of
+// offsets (one XOR per read).  Bases may be offset by any multiple of the
+// tile size: the XORs only touch bits below it.
+template <int D>
+__device__ __forceinline__ uint32_t tile_row_base(int r, int h) { return 2 * tile_off<D>(r, 8 * h); }
+template <int D>
+__device__ __forceinline__ uint32_t tile_tr_base(int r0, int c0) { return 2 * tile_off<D>(r0, c0); }
+template <int D>
+__device__ __forceinline__ uint32_t tile_tr_xor(int t, int nb) { return 2 * tile_off<D>(8 * t, 32 * nb); }
+
+template <typename V>
+__device__ __forceinline__ V lds_at(const void* tile, uint32_t byte_off) {
+  return *reinterpret_cast<const V*>(reinterpret_cast<const char*>(tile) + byte_off);
+}
+__device__ __forceinline__ u32x2 lds_tr_at(const void* tile, uint32_t byte_off) {
+  return lds_read_tr16(reinterpret_cast<const char*>(tile) + byte_off);
+}
+
 // Direct global-to-LDS load of rows kb .. kb + BC - 1 of a head into the tile
 // at dst by NW waves: the tile is cut into 1 KiB segments, wave w fills
 // segments w SPW .. w SPW + SPW - 1, and lane l of segment g fills LDS chunk
