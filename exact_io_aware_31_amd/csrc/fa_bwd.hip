@@ -370,43 +370,58 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
       // into sixteen loop-invariant registers.
       uint32_t rbs = rb, tbs = tb;
       asm volatile("" : "+v"(rbs), "+v"(tbs));
-      v8 dsb[BC / 16];
+      // Both halves' S and dP first, then one mask branch (taken on diagonal
+      // and ragged tiles only), then per 32 keys the exponentials and dS
+      // followed by that half's dQ products: the second half's VALU work can
+      // then run beside the first half's dQ MFMAs.
+      {
+        f32x16 s[BC / 32], dp[BC / 32];
 #pragma unroll
-      for (int sb = 0; sb < BC / 32; ++sb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        for (int sb = 0; sb < BC / 32; ++sb) {
+          s[sb] = f32x16{};
+          dp[sb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const v8 ak = lds_at<v8>(kt, (rbs ^ (32 * kk)) + 64 * D * sb);
-          const v8 av = lds_at<v8>(vt, (rbs ^ (32 * kk)) + 64 * D * sb);
-          s = mfma32x32x16(ak, qf[kk], s);
-          dp = mfma32x32x16(av, dof[kk], dp);
+          for (int kk = 0; kk < D / 16; ++kk) {
+            const v8 ak = lds_at<v8>(kt, (rbs ^ (32 * kk)) + 64 * D * sb);
+            const v8 av = lds_at<v8>(vt, (rbs ^ (32 * kk)) + 64 * D * sb);
+            s[sb] = mfma32x32x16(ak, qf[kk], s[sb]);
+            dp[sb] = mfma32x32x16(av, dof[kk], dp[sb]);
+          }
         }
         if (need_mask) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * sb + 8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
+          for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * sb + 8 * (r >> 2) + (r & 3) > lim) s[sb][r] = -INFINITY;
         }
+        // Per 32 keys: dS^T = P^T o (dP^T - D), then dQ^T += K^T dS^T for
+        // those keys (K^T from two transpose reads per MFMA).
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          float dsv[8];
+        for (int sb = 0; sb < BC / 32; ++sb) {
+          v8 dsb[2];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * hf + e;
-            dsv[e] = fast_exp2(__builtin_fmaf(s[r], c, -lq)) * (dp[r] - dq_row);
+          for (int hf = 0; hf < 2; ++hf) {
+            float dsv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * hf + e;
+              dsv[e] = fast_exp2(__builtin_fmaf(s[sb][r], c, -lq)) * (dp[sb][r] - dq_row);
+            }
+            dsb[hf] = to_v8<T>(dsv);
           }
-          dsb[2 * sb + hf] = to_v8<T>(dsv);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const int kc = 2 * sb + hf;
+              const u32x2 lo = lds_tr_at(kt, (tbs ^ tile_tr_xor<D>(0, nb)) + 32 * D * kc);
+              const u32x2 hi = lds_tr_at(kt, (tbs ^ tile_tr_xor<D>(1, nb)) + 32 * D * kc);
+              const u32x4 cat = {lo[0], lo[1], hi[0], hi[1]};
+              dqacc[nb] = mfma32x32x16(__builtin_bit_cast(v8, cat), dsb[hf], dqacc[nb]);
+            }
         }
       }
-      // dQ^T += K^T dS^T; the K^T operand comes from two transpose reads.
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int kc = 0; kc < BC / 16; ++kc) {
-          const u32x2 lo = lds_tr_at(kt, (tbs ^ tile_tr_xor<D>(0, nb)) + 32 * D * kc);
-          const u32x2 hi = lds_tr_at(kt, (tbs ^ tile_tr_xor<D>(1, nb)) + 32 * D * kc);
-          const u32x4 cat = {lo[0], lo[1], hi[0], hi[1]};
-          dqacc[nb] = mfma32x32x16(__builtin_bit_cast(v8, cat), dsb[kc], dqacc[nb]);
-        }
     }
     // Tile j+1 has landed (this wave's share) and every LDS read of tile j
     // has returned; after the barrier no wave reads tile j's buffer again.
