@@ -11,7 +11,9 @@ numpy arrays or torch tensors of any float dtype; they are widened exactly
 to float64 (fp16 and bf16 values are exactly representable in float64).
 
 Shapes follow the attention problem statement: q, k, v are [..., N, d]
-(leading dims are flattened into independent heads).
+(leading dims are flattened into independent heads).  Grouped key/value
+heads: q [..., H, N, d] with k, v [..., H_kv, N, d], H a multiple of H_kv;
+query head h reads key/value head h // (H / H_kv).
 
 Parity status: every function is pinned by tests/test_oracle.py against
 values printed on the pages, closed forms, invariants, finite differences
@@ -53,6 +55,16 @@ def _load():
     lib.oracle_attn_decode.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_long, ctypes.c_long,
                                        ctypes.c_long, ctypes.c_double, ctypes.c_int]
     lib.oracle_attn_decode.restype = ctypes.c_int
+    L = ctypes.c_long
+    lib.oracle_attn_fwd_w.argtypes = [_dp, _dp, _dp, _dp, _dp, L, L, L, L, L, L, ctypes.c_double,
+                                      ctypes.c_int, L, _lp, ctypes.c_int]
+    lib.oracle_attn_fwd_w.restype = ctypes.c_int
+    lib.oracle_attn_decode_w.argtypes = [_dp, _dp, _dp, _dp, _dp, L, L, L, L, L, ctypes.c_double,
+                                         ctypes.c_int]
+    lib.oracle_attn_decode_w.restype = ctypes.c_int
+    lib.oracle_attn_bwd_w.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, L, L, L, L, L,
+                                      ctypes.c_double, ctypes.c_int, L, ctypes.c_int]
+    lib.oracle_attn_bwd_w.restype = ctypes.c_int
     lib.oracle_attn_fwd_tiled.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_long,
                                           ctypes.c_long, ctypes.c_long, ctypes.c_double,
                                           ctypes.c_int, ctypes.c_long, ctypes.c_long]
@@ -107,14 +119,28 @@ def softmax_online(x, chunk: int):
     return p, mt[:got], lt[:got]
 
 
-def attn_fwd(q, k, v, scale: float, causal: bool, qpos=None, nthreads: int = 0):
-    """Three-step attention.  q [..., nq, d], k/v [..., nk, d] -> (o, lse)."""
+def _heads(qlead, klead):
+    """(B, H, H_kv) for leading dims of q [..., H, ., d] and k [..., H_kv, ., d]."""
+    if tuple(qlead) == tuple(klead):
+        bh = int(np.prod(qlead)) if qlead else 1
+        return 1, bh, bh
+    assert len(qlead) >= 1 and tuple(qlead[:-1]) == tuple(klead[:-1]), "batch dims differ"
+    assert qlead[-1] % klead[-1] == 0, "query heads must be a multiple of key/value heads"
+    return int(np.prod(qlead[:-1])) if len(qlead) > 1 else 1, int(qlead[-1]), int(klead[-1])
+
+
+def attn_fwd(q, k, v, scale: float, causal: bool, qpos=None, nthreads: int = 0,
+             window: int = 0):
+    """Three-step attention.  q [..., nq, d], k/v [..., nk, d] -> (o, lse).
+
+    window > 0 (with causal): key j visible to query i iff i - window < j <= i.
+    k and v may have fewer heads than q (grouped-query attention)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     lead = q.shape[:-2]
     nq, d = q.shape[-2:]
     nk = k.shape[-2]
-    assert k.shape[:-2] == lead and v.shape == k.shape and k.shape[-1] == d
-    bh = int(np.prod(lead)) if lead else 1
+    assert v.shape == k.shape and k.shape[-1] == d
+    b, h, hkv = _heads(lead, k.shape[:-2])
     o = np.empty(q.shape)
     lse = np.empty(lead + (nq,))
     qp = None
@@ -122,10 +148,11 @@ def attn_fwd(q, k, v, scale: float, causal: bool, qpos=None, nthreads: int = 0):
         qp_arr = np.ascontiguousarray(np.asarray(qpos, dtype=np.int64))
         assert qp_arr.shape == (nq,)
         qp = qp_arr.ctypes.data_as(_lp)
-    rc = _load().oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), bh, nq, nk, d,
-                                 float(scale), int(bool(causal)), qp, int(nthreads))
+    rc = _load().oracle_attn_fwd_w(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, h, hkv, nq,
+                                   nk, d, float(scale), int(bool(causal)), int(window), qp,
+                                   int(nthreads))
     if rc != 0:
-        raise RuntimeError(f"oracle_attn_fwd failed ({rc})")
+        raise RuntimeError(f"oracle_attn_fwd_w failed ({rc})")
     return o, lse
 
 
@@ -144,18 +171,25 @@ def attn_fwd_tiled(q, k, v, scale: float, causal: bool, br: int, bc: int):
 
 
 def attn_decode(q, k, v, scale: float, nthreads: int = 0):
-    """Single-token decode.  q [..., d] (or [..., 1, d]), k/v [..., nkv, d]."""
+    """Single-token decode.  q [..., H, d] (or [..., H, 1, d]), k/v [..., H_kv, nkv, d]
+    (H_kv may divide H); returns o [..., H, d] and lse [..., H]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
-    lead = k.shape[:-2]
     nkv, d = k.shape[-2:]
-    q = q.reshape(lead + (d,))
-    bh = int(np.prod(lead)) if lead else 1
-    o = np.empty(lead + (d,))
-    lse = np.empty(lead)
-    rc = _load().oracle_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), bh, nkv, d,
-                                    float(scale), int(nthreads))
+    klead = k.shape[:-2]
+    if k.ndim >= 3:
+        batch, hkv = klead[:-1], int(klead[-1])
+    else:
+        batch, hkv = (), 1
+    b = int(np.prod(batch)) if batch else 1
+    h = q.size // d // b
+    assert h * b * d == q.size and h % hkv == 0
+    q = q.reshape(b * h, d)
+    o = np.empty(batch + (h, d)) if k.ndim >= 3 else np.empty((d,))
+    lse = np.empty(batch + (h,)) if k.ndim >= 3 else np.empty(())
+    rc = _load().oracle_attn_decode_w(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, h, hkv,
+                                      nkv, d, float(scale), int(nthreads))
     if rc != 0:
-        raise RuntimeError(f"oracle_attn_decode failed ({rc})")
+        raise RuntimeError(f"oracle_attn_decode_w failed ({rc})")
     return o, lse
 
 
@@ -172,20 +206,21 @@ def lse_merge(o_parts, lse_parts):
 
 
 def attn_bwd(q, k, v, dout, scale: float, causal: bool, return_drow: bool = False,
-             nthreads: int = 0):
-    """Gradients of the three-step definition.  All of shape [..., n, d]."""
+             nthreads: int = 0, window: int = 0):
+    """Gradients of the three-step definition.  q, dout [..., n, d]; k, v [..., n, d]
+    with possibly fewer heads than q (their gradients sum over each group)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
     lead = q.shape[:-2]
     n, d = q.shape[-2:]
-    assert k.shape == q.shape and v.shape == q.shape and do.shape == q.shape
-    bh = int(np.prod(lead)) if lead else 1
-    dq, dk, dv = np.empty(q.shape), np.empty(q.shape), np.empty(q.shape)
+    assert v.shape == k.shape and k.shape[-2:] == (n, d) and do.shape == q.shape
+    b, h, hkv = _heads(lead, k.shape[:-2])
+    dq, dk, dv = np.empty(q.shape), np.empty(k.shape), np.empty(k.shape)
     drow = np.empty(lead + (n,))
-    rc = _load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
-                                 _ptr(dv), _ptr(drow), bh, n, d, float(scale),
-                                 int(bool(causal)), int(nthreads))
+    rc = _load().oracle_attn_bwd_w(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _ptr(drow), b, h, hkv, n, d, float(scale),
+                                   int(bool(causal)), int(window), int(nthreads))
     if rc != 0:
-        raise RuntimeError(f"oracle_attn_bwd failed ({rc})")
+        raise RuntimeError(f"oracle_attn_bwd_w failed ({rc})")
     if return_drow:
         return dq, dk, dv, drow
     return dq, dk, dv

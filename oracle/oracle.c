@@ -21,6 +21,12 @@
  * Readings taken where the pages are silent (each also listed in the design
  * notes of the repository):
  *   - causal: key j is visible to query i iff j <= i (pages say "mask" only);
+ *   - sliding window w > 0 (with causal): key j is visible to query i iff
+ *     i - w < j <= i, the w most recent keys including the query's own
+ *     position (the pages name the variant, not its formula);
+ *   - grouped-query attention: H query heads share H_kv key/value heads in
+ *     contiguous groups, query head h reading key/value head h / (H / H_kv)
+ *     (the pages say several query heads share one key/value head);
  *   - lse: the natural-log log-sum-exp of the scaled, masked scores of a row,
  *     lse = m + ln(l);  a row with no visible key gets O = 0, lse = -inf;
  *   - scale multiplies Q K^T before masking and softmax (pages fix 1/sqrt(d));
@@ -37,7 +43,16 @@
 
 #define ORACLE_ROWS_PER_TASK 32
 
-static int oracle_visible(long i, long j, int causal) { return !causal || j <= i; }
+/*
+ * Visibility of key j from query i.  Causal masking [P4 Step 2 lists the mask
+ * among the per-element operations]; the sliding window restricts the keys to
+ * the window [P3 §"Variantes et extensions", sliding-window variant].
+ */
+static int oracle_visible(long i, long j, int causal, long window) {
+  if (!causal) return 1;
+  if (j > i) return 0;
+  return window <= 0 || j > i - window;
+}
 
 static void oracle_set_threads(int nthreads) {
   if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -109,14 +124,14 @@ long oracle_softmax_online(const double* x, long n, long chunk, double* p,
  */
 static void oracle_fwd_rows(const double* q, const long* qpos, long r0, long r1,
                             const double* k, const double* v, long nk, long d,
-                            double scale, int causal, double* o, double* lse,
+                            double scale, int causal, long window, double* o, double* lse,
                             double* s, double* p) {
   /* step 1: S = scale * Q K^T, masked entries = -inf */
   for (long r = r0; r < r1; ++r) {
     long i = qpos ? qpos[r] : r;
     double* srow = s + (r - r0) * nk;
     for (long j = 0; j < nk; ++j) {
-      if (!oracle_visible(i, j, causal)) { srow[j] = -INFINITY; continue; }
+      if (!oracle_visible(i, j, causal, window)) { srow[j] = -INFINITY; continue; }
       double acc = 0.0;
       for (long c = 0; c < d; ++c) acc += q[r * d + c] * k[j * d + c];
       srow[j] = scale * acc;
@@ -147,17 +162,22 @@ static void oracle_fwd_rows(const double* q, const long* qpos, long r0, long r1,
 }
 
 /*
- * Forward over BH heads.  q [BH, nq, d]; k, v [BH, nk, d]; o [BH, nq, d];
- * lse [BH, nq].  qpos (may be NULL) applies to every head.  Independent
- * (head, row block) tasks run in parallel.
+ * Forward over B x H query heads.  q [B, H, nq, d]; k, v [B, Hkv, nk, d];
+ * o [B, H, nq, d]; lse [B, H, nq].  Query head h of batch b reads key/value
+ * head b * Hkv + h / (H / Hkv) (Hkv = H is plain multi-head attention).
+ * qpos (may be NULL) applies to every head.  Independent (head, row block)
+ * tasks run in parallel.
  */
-int oracle_attn_fwd(const double* q, const double* k, const double* v,
-                    double* o, double* lse, long BH, long nq, long nk, long d,
-                    double scale, int causal, const long* qpos, int nthreads) {
-  if (!q || !k || !v || !o || !lse || BH < 0 || nq < 0 || nk < 0 || d <= 0) return 1;
+int oracle_attn_fwd_w(const double* q, const double* k, const double* v,
+                      double* o, double* lse, long B, long H, long Hkv, long nq, long nk,
+                      long d, double scale, int causal, long window, const long* qpos,
+                      int nthreads) {
+  if (!q || !k || !v || !o || !lse || B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || nq < 0 ||
+      nk < 0 || d <= 0)
+    return 1;
   oracle_set_threads(nthreads);
   long nblk = (nq + ORACLE_ROWS_PER_TASK - 1) / ORACLE_ROWS_PER_TASK;
-  long ntask = BH * nblk;
+  long ntask = B * H * nblk;
   int failed = 0;
 #pragma omp parallel
   {
@@ -170,15 +190,26 @@ int oracle_attn_fwd(const double* q, const double* k, const double* v,
 #pragma omp for schedule(dynamic)
     for (long t = 0; t < ntask; ++t) {
       if (!s || !p) continue;
-      long h = t / nblk, r0 = (t % nblk) * ORACLE_ROWS_PER_TASK;
+      long qh = t / nblk, r0 = (t % nblk) * ORACLE_ROWS_PER_TASK;
+      long b = qh / H, h = qh % H;
+      long kvh = b * Hkv + h / (H / Hkv);
       long r1 = r0 + ORACLE_ROWS_PER_TASK < nq ? r0 + ORACLE_ROWS_PER_TASK : nq;
-      oracle_fwd_rows(q + h * nq * d, qpos, r0, r1, k + h * nk * d, v + h * nk * d, nk, d,
-                      scale, causal, o + h * nq * d, lse + h * nq, s, p);
+      oracle_fwd_rows(q + qh * nq * d, qpos, r0, r1, k + kvh * nk * d, v + kvh * nk * d, nk, d,
+                      scale, causal, window, o + qh * nq * d, lse + qh * nq, s, p);
     }
     free(s);
     free(p);
   }
   return failed ? 2 : 0;
+}
+
+/* Forward over BH independent heads (multi-head, no window). */
+int oracle_attn_fwd(const double* q, const double* k, const double* v,
+                    double* o, double* lse, long BH, long nq, long nk, long d,
+                    double scale, int causal, const long* qpos, int nthreads) {
+  if (BH == 0) return (!q || !k || !v || !o || !lse || nq < 0 || nk < 0 || d <= 0) ? 1 : 0;
+  return oracle_attn_fwd_w(q, k, v, o, lse, 1, BH, BH, nq, nk, d, scale, causal, 0, qpos,
+                           nthreads);
 }
 
 /*
@@ -192,6 +223,13 @@ int oracle_attn_decode(const double* q, const double* k, const double* v,
                        double* o, double* lse, long BH, long nkv, long d,
                        double scale, int nthreads) {
   return oracle_attn_fwd(q, k, v, o, lse, BH, 1, nkv, d, scale, 0, NULL, nthreads);
+}
+
+/* Decode with grouped key/value heads: q [B, H, d]; k, v [B, Hkv, nkv, d]. */
+int oracle_attn_decode_w(const double* q, const double* k, const double* v,
+                         double* o, double* lse, long B, long H, long Hkv, long nkv, long d,
+                         double scale, int nthreads) {
+  return oracle_attn_fwd_w(q, k, v, o, lse, B, H, Hkv, 1, nkv, d, scale, 0, 0, NULL, nthreads);
 }
 
 /*
@@ -225,7 +263,7 @@ int oracle_attn_fwd_tiled(const double* q, const double* k, const double* v,
         double rowmax = -INFINITY;
         for (long j = j0; j < j1; ++j) {
           double acc = -INFINITY;
-          if (oracle_visible(r, j, causal)) {
+          if (oracle_visible(r, j, causal, 0)) {
             acc = 0.0;
             for (long c = 0; c < d; ++c) acc += q[r * d + c] * k[j * d + c];
             acc *= scale;
@@ -311,7 +349,7 @@ int oracle_lse_merge(const double* o_parts, const double* lse_parts, long nparts
  */
 static void oracle_bwd_head(const double* q, const double* k, const double* v,
                             const double* dout, double* dq, double* dk, double* dv,
-                            double* drow, long n, long d, double scale, int causal,
+                            double* drow, long n, long d, double scale, int causal, long window,
                             double* P, double* dS) {
   /* rebuild P row by row from its definition */
 #pragma omp parallel
@@ -320,7 +358,7 @@ static void oracle_bwd_head(const double* q, const double* k, const double* v,
 #pragma omp for schedule(dynamic, 16)
     for (long i = 0; i < n; ++i) {
       for (long j = 0; j < n; ++j) {
-        if (!oracle_visible(i, j, causal)) { srow[j] = -INFINITY; continue; }
+        if (!oracle_visible(i, j, causal, window)) { srow[j] = -INFINITY; continue; }
         double acc = 0.0;
         for (long c = 0; c < d; ++c) acc += q[i * d + c] * k[j * d + c];
         srow[j] = scale * acc;
@@ -335,7 +373,7 @@ static void oracle_bwd_head(const double* q, const double* k, const double* v,
     double* dsrow = dS + i * n;
     for (long j = 0; j < n; ++j) {
       double acc = 0.0;
-      if (oracle_visible(i, j, causal))
+      if (oracle_visible(i, j, causal, window))
         for (long c = 0; c < d; ++c) acc += dout[i * d + c] * v[j * d + c];
       dsrow[j] = acc; /* dP for now */
     }
@@ -371,25 +409,52 @@ static void oracle_bwd_head(const double* q, const double* k, const double* v,
 }
 
 /*
- * Backward over BH heads.  q, k, v, dout, dq, dk, dv: [BH, n, d];
- * drow (may be NULL): [BH, n], receives D_i = sum_j P_ij dP_ij.
+ * Backward over B x H query heads with grouped key/value heads.
+ * q, dout, dq: [B, H, n, d]; k, v, dk, dv: [B, Hkv, n, d]; drow (may be
+ * NULL): [B, H, n].  A key/value head is an input of each query head of its
+ * group, so its gradient is the sum of the group's per-head gradients
+ * (chain rule), added here in head order.
  * Returns 0 on success, 1 on bad arguments, 2 if scratch allocation failed.
  */
+int oracle_attn_bwd_w(const double* q, const double* k, const double* v,
+                      const double* dout, double* dq, double* dk, double* dv,
+                      double* drow, long B, long H, long Hkv, long n, long d, double scale,
+                      int causal, long window, int nthreads) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv || B < 0 || H < 1 || Hkv < 1 ||
+      H % Hkv != 0 || n < 0 || d <= 0)
+    return 1;
+  oracle_set_threads(nthreads);
+  double* P = (double*)malloc(sizeof(double) * (size_t)n * (size_t)n + 8);
+  double* dS = (double*)malloc(sizeof(double) * (size_t)n * (size_t)n + 8);
+  double* gk = (double*)malloc(sizeof(double) * (size_t)n * (size_t)d + 8);
+  double* gv = (double*)malloc(sizeof(double) * (size_t)n * (size_t)d + 8);
+  if (!P || !dS || !gk || !gv) { free(P); free(dS); free(gk); free(gv); return 2; }
+  memset(dk, 0, sizeof(double) * (size_t)(B * Hkv) * n * d);
+  memset(dv, 0, sizeof(double) * (size_t)(B * Hkv) * n * d);
+  for (long b = 0; b < B; ++b)
+    for (long h = 0; h < H; ++h) {
+      size_t qoff = (size_t)(b * H + h) * n * d;
+      size_t kvoff = (size_t)(b * Hkv + h / (H / Hkv)) * n * d;
+      oracle_bwd_head(q + qoff, k + kvoff, v + kvoff, dout + qoff, dq + qoff, gk, gv,
+                      drow ? drow + (b * H + h) * n : NULL, n, d, scale, causal, window, P, dS);
+      for (long e = 0; e < n * d; ++e) {
+        dk[kvoff + e] += gk[e];
+        dv[kvoff + e] += gv[e];
+      }
+    }
+  free(P);
+  free(dS);
+  free(gk);
+  free(gv);
+  return 0;
+}
+
+/* Backward over BH independent heads (multi-head, no window). */
 int oracle_attn_bwd(const double* q, const double* k, const double* v,
                     const double* dout, double* dq, double* dk, double* dv,
                     double* drow, long BH, long n, long d, double scale, int causal,
                     int nthreads) {
-  if (!q || !k || !v || !dout || !dq || !dk || !dv || BH < 0 || n < 0 || d <= 0) return 1;
-  oracle_set_threads(nthreads);
-  double* P = (double*)malloc(sizeof(double) * (size_t)n * (size_t)n + 8);
-  double* dS = (double*)malloc(sizeof(double) * (size_t)n * (size_t)n + 8);
-  if (!P || !dS) { free(P); free(dS); return 2; }
-  for (long h = 0; h < BH; ++h) {
-    size_t off = (size_t)h * n * d;
-    oracle_bwd_head(q + off, k + off, v + off, dout + off, dq + off, dk + off, dv + off,
-                    drow ? drow + h * n : NULL, n, d, scale, causal, P, dS);
-  }
-  free(P);
-  free(dS);
-  return 0;
+  if (BH == 0) return (!q || !k || !v || !dout || !dq || !dk || !dv || n < 0 || d <= 0) ? 1 : 0;
+  return oracle_attn_bwd_w(q, k, v, dout, dq, dk, dv, drow, 1, BH, BH, n, d, scale, causal, 0,
+                           nthreads);
 }

@@ -285,6 +285,159 @@ def test_bwd_causal_last_key_gets_only_last_query():
 
 
 # --------------------------------------------------------------------------
+# Sliding window ("03. FlashAttention", § "Variantes et extensions": the
+# variant only considers the keys inside the window; reading: key j is
+# visible to query i iff i - w < j <= i)
+# --------------------------------------------------------------------------
+
+def window_mask(n, w):
+    """Boolean [n, n] mask built from band matrices (lower triangle minus the
+    part more than w - 1 below the diagonal)."""
+    ones = np.ones((n, n), dtype=bool)
+    return np.tril(ones) & ~np.tril(ones, -w)
+
+
+@pytest.mark.parametrize("n,d,w", [(9, 4, 3), (40, 8, 7), (64, 16, 1), (33, 8, 32)])
+def test_window_fwd_bwd_match_torch_masked_sdpa(n, d, w):
+    q, k, v, do = (rand(2, 2, n, d) for _ in range(4))
+    scale = 1 / math.sqrt(d)
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_() for a in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=torch.from_numpy(window_mask(n, w)), scale=scale)
+    o.backward(torch.from_numpy(do))
+    got, _ = oracle.attn_fwd(q, k, v, scale, True, window=w)
+    assert np.max(np.abs(got - o.detach().numpy())) <= 1e-13
+    for g, t in zip(oracle.attn_bwd(q, k, v, do, scale, True, window=w), (tq, tk, tv)):
+        assert np.max(np.abs(g - t.grad.numpy())) <= 1e-12
+
+
+@pytest.mark.parametrize("w", [1, 2, 5, 11])
+def test_window_rows_are_unmasked_attention_over_their_keys(w):
+    n, d = 23, 8
+    q, k, v = rand(n, d), rand(n, d), rand(n, d)
+    o, lse = oracle.attn_fwd(q, k, v, 0.4, True, window=w)
+    for i in range(n):
+        lo = max(0, i - w + 1)
+        oi, li = oracle.attn_fwd(q[i:i + 1], k[lo:i + 1], v[lo:i + 1], 0.4, False)
+        assert np.max(np.abs(o[i] - oi[0])) <= 1e-14 and abs(lse[i] - li[0]) <= 1e-14
+
+
+def test_window_one_closed_form():
+    n, d = 17, 8
+    q, k, v, do = rand(n, d), rand(n, d), rand(n, d), rand(n, d)
+    o, lse = oracle.attn_fwd(q, k, v, 0.7, True, window=1)
+    # each query sees only its own key: O = V, lse = scale q_i . k_i
+    assert np.array_equal(o, v)
+    assert np.max(np.abs(lse - 0.7 * np.sum(q * k, axis=1))) <= 1e-14
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, 0.7, True, window=1)
+    # P = 1 on the diagonal, so dS = P (dP - D) vanishes and dV = dO
+    assert np.array_equal(dv, do) and not np.any(dq) and not np.any(dk)
+
+
+@pytest.mark.parametrize("w", [40, 41, 1000])
+def test_window_covering_the_sequence_is_causal(w):
+    n, d = 40, 8
+    q, k, v, do = rand(n, d), rand(n, d), rand(n, d), rand(n, d)
+    a = oracle.attn_fwd(q, k, v, 0.5, True, window=w)
+    c = oracle.attn_fwd(q, k, v, 0.5, True)
+    assert all(np.array_equal(x, y) for x, y in zip(a, c))
+    ga = oracle.attn_bwd(q, k, v, do, 0.5, True, window=w)
+    gc = oracle.attn_bwd(q, k, v, do, 0.5, True)
+    assert all(np.array_equal(x, y) for x, y in zip(ga, gc))
+
+
+@pytest.mark.parametrize("w", [2, 4])
+def test_window_bwd_finite_differences(w):
+    n, d = 7, 3
+    q, k, v, do = rand(n, d), rand(n, d), rand(n, d), rand(n, d)
+    scale = 0.6
+    got = oracle.attn_bwd(q, k, v, do, scale, True, window=w)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attn_fwd(qq, kk, vv, scale, True, window=w)
+        return float(np.sum(o * do))
+    for idx, g in enumerate(got):
+        x0 = (q, k, v)[idx]
+        ref = np.zeros_like(x0)
+        for pos in np.ndindex(x0.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[idx][pos] += 1e-6
+            up = loss(*args)
+            args[idx][pos] -= 2e-6
+            ref[pos] = (up - loss(*args)) / 2e-6
+        assert np.linalg.norm(g - ref) <= 1e-6 * max(np.linalg.norm(ref), 1e-3)
+
+
+# --------------------------------------------------------------------------
+# Grouped key/value heads ("FlashAttention ontleed", § "Interactie met de
+# KV-cache tijdens inferentie": several query heads share one key/value head;
+# reading: query head h reads key/value head h // (H / H_kv))
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("h,hkv,causal", [(4, 2, True), (6, 3, False), (8, 1, True), (4, 4, False)])
+def test_gqa_fwd_bwd_match_torch_sdpa(h, hkv, causal):
+    b, n, d = 2, 19, 8
+    q, do = rand(b, h, n, d), rand(b, h, n, d)
+    k, v = rand(b, hkv, n, d), rand(b, hkv, n, d)
+    scale = 1 / math.sqrt(d)
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_() for a in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale,
+                                                         enable_gqa=True)
+    o.backward(torch.from_numpy(do))
+    got, _ = oracle.attn_fwd(q, k, v, scale, causal)
+    assert np.max(np.abs(got - o.detach().numpy())) <= 1e-13
+    for g, t in zip(oracle.attn_bwd(q, k, v, do, scale, causal), (tq, tk, tv)):
+        assert g.shape == t.shape and np.max(np.abs(g - t.grad.numpy())) <= 1e-12
+
+
+def test_gqa_heads_are_plain_attention_on_their_group_head():
+    b, h, hkv, n, d = 2, 6, 2, 13, 8
+    q, do = rand(b, h, n, d), rand(b, h, n, d)
+    k, v = rand(b, hkv, n, d), rand(b, hkv, n, d)
+    o, lse = oracle.attn_fwd(q, k, v, 0.5, True, window=5)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, 0.5, True, window=5)
+    g = h // hkv
+    sk, sv = np.zeros_like(k), np.zeros_like(v)
+    for bi in range(b):
+        for hi in range(h):
+            kv = hi // g
+            oh, lh = oracle.attn_fwd(q[bi, hi], k[bi, kv], v[bi, kv], 0.5, True, window=5)
+            assert np.array_equal(oh, o[bi, hi]) and np.array_equal(lh, lse[bi, hi])
+            gq, gk, gv = oracle.attn_bwd(q[bi, hi], k[bi, kv], v[bi, kv], do[bi, hi], 0.5, True,
+                                         window=5)
+            assert np.array_equal(gq, dq[bi, hi])
+            sk[bi, kv] += gk
+            sv[bi, kv] += gv
+    # a shared head's gradient is the sum of its group's per-head gradients
+    assert np.max(np.abs(sk - dk)) <= 1e-14 and np.max(np.abs(sv - dv)) <= 1e-14
+
+
+def test_gqa_identical_query_heads_scale_the_shared_gradient():
+    n, d, g = 11, 4, 3
+    q1, do1 = rand(n, d), rand(n, d)
+    k, v = rand(1, 1, n, d), rand(1, 1, n, d)
+    q = np.broadcast_to(q1, (1, g, n, d)).copy()
+    do = np.broadcast_to(do1, (1, g, n, d)).copy()
+    _, dk, dv = oracle.attn_bwd(q, k, v, do, 0.5, False)
+    _, dk1, dv1 = oracle.attn_bwd(q1, k[0, 0], v[0, 0], do1, 0.5, False)
+    assert np.max(np.abs(dk[0, 0] - g * dk1)) <= 1e-13
+    assert np.max(np.abs(dv[0, 0] - g * dv1)) <= 1e-13
+
+
+def test_gqa_decode_matches_torch():
+    b, h, hkv, nkv, d = 2, 8, 2, 200, 16
+    q, k, v = rand(b, h, 1, d), rand(b, hkv, nkv, d), rand(b, hkv, nkv, d)
+    o, lse = oracle.attn_decode(q, k, v, 0.25)
+    t = [torch.from_numpy(a) for a in (q, k, v)]
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, scale=0.25, enable_gqa=True)
+    assert o.shape == (b, h, d) and lse.shape == (b, h)
+    assert np.max(np.abs(o - ref.numpy()[:, :, 0])) <= 1e-13
+    ref_lse = scipy.special.logsumexp(0.25 * np.einsum("bhd,bhnd->bhn", q[:, :, 0],
+                                                       np.repeat(k, h // hkv, axis=1)), axis=-1)
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-13
+
+
+# --------------------------------------------------------------------------
 # Decode and the split-history merge
 # --------------------------------------------------------------------------
 

@@ -16,8 +16,15 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 # (name, original text, planted mistake); each original must occur in oracle.c
 MUTANTS = [
-    ("mask_reversed", "return !causal || j <= i;", "return !causal || j >= i;"),
-    ("mask_off_by_one", "return !causal || j <= i;", "return !causal || j < i;"),
+    ("mask_reversed", "if (j > i) return 0;", "if (j < i) return 0;"),
+    ("mask_off_by_one", "if (j > i) return 0;", "if (j >= i) return 0;"),
+    ("window_off_by_one", "return window <= 0 || j > i - window;",
+     "return window <= 0 || j >= i - window;"),
+    ("window_ignored", "return window <= 0 || j > i - window;", "return 1;"),
+    ("gqa_fwd_heads_interleaved", "long kvh = b * Hkv + h / (H / Hkv);", "long kvh = b * Hkv + h % Hkv;"),
+    ("gqa_bwd_heads_interleaved", "size_t kvoff = (size_t)(b * Hkv + h / (H / Hkv)) * n * d;",
+     "size_t kvoff = (size_t)(b * Hkv + h % Hkv) * n * d;"),
+    ("gqa_bwd_no_group_sum", "dk[kvoff + e] += gk[e];", "dk[kvoff + e] = gk[e];"),
     ("no_max_subtraction", "for (long i = 0; i < n; ++i) p[i] = exp(x[i] - m) / s;",
      "for (long i = 0; i < n; ++i) p[i] = exp(x[i]) / (s * exp(m));"),
     ("online_drops_rescale", "l = l * rescale + csum;", "l = l + csum;"),
