@@ -9,6 +9,9 @@ Low-level functions carry the C names and take caller-allocated tensors:
     fa_fwd(q, k, v, o, lse, scale, causal)
     fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, causal)
     fa_decode(q, k, v, o, lse, scale, num_splits, workspace)
+    fa_fwd_ex / fa_bwd_ex / fa_decode_ex: the same with grouped key/value heads
+        (k, v with H_kv heads dividing H) and, forward and backward, a causal
+        sliding window (window=w: key j visible to query i iff i - w < j <= i)
     fa_bwd_workspace_bytes(B, H, N, d), fa_decode_workspace_bytes(B, H, d, S)
     fa_status_string(code), fa_version()
 Convenience wrappers allocate outputs and workspaces with torch:
@@ -57,6 +60,13 @@ def load_library(path: str = LIB_PATH):
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, i, vp]
     lib.fa_decode.restype = i
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_fwd_ex.restype = i
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i,
+                              i, vp]
+    lib.fa_bwd_ex.restype = i
+    lib.fa_decode_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, i, vp]
+    lib.fa_decode_ex.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -159,18 +169,77 @@ def fa_decode(q, k, v, o, lse, scale: float, num_splits: int, workspace, stream=
                                     _stream(k, stream)), "fa_decode")
 
 
+def _kv_heads(q, k) -> int:
+    B, H = q.shape[0], q.shape[1]
+    if k.dim() != 4 or k.shape[0] != B or k.shape[-1] != q.shape[-1]:
+        raise ValueError(f"k has shape {tuple(k.shape)}; expected [B, H_kv, N, d] for q "
+                         f"{tuple(q.shape)}")
+    hkv = k.shape[1]
+    if hkv < 1 or H % hkv != 0:
+        raise ValueError(f"query heads {H} are not a multiple of key/value heads {hkv}")
+    return hkv
+
+
+def fa_fwd_ex(q, k, v, o, lse, scale: float, causal: bool, window: int = 0, stream=None):
+    """fa_fwd with k, v of H_kv heads ([B, H_kv, N, d]) and an optional causal window."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    hkv = _kv_heads(q, k)
+    kv = (B, hkv, N, d)
+    args = [_dev(q, "q"), _dev(k, "k", q.dtype, kv), _dev(v, "v", q.dtype, kv),
+            _dev(o, "o", q.dtype, q.shape), _dev(lse, "lse", torch.float32, (B, H, N))]
+    _check(load_library().fa_fwd_ex(*args, B, H, hkv, N, d, float(scale), int(bool(causal)),
+                                    int(window), _dt_code(q), _stream(q, stream)), "fa_fwd_ex")
+
+
+def fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale: float, causal: bool,
+              window: int = 0, stream=None):
+    """fa_bwd with k, v, dk, dv of H_kv heads and an optional causal window."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    hkv = _kv_heads(q, k)
+    sh, kv = q.shape, (B, hkv, N, d)
+    args = [_dev(q, "q"), _dev(k, "k", q.dtype, kv), _dev(v, "v", q.dtype, kv),
+            _dev(o, "o", q.dtype, sh), _dev(lse, "lse", torch.float32, (B, H, N)),
+            _dev(dout, "dout", q.dtype, sh), _dev(dq, "dq", q.dtype, sh),
+            _dev(dk, "dk", q.dtype, kv), _dev(dv, "dv", q.dtype, kv), _dev(workspace, "workspace")]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fa_bwd_ex(*args, nbytes, B, H, hkv, N, d, float(scale),
+                                    int(bool(causal)), int(window), _dt_code(q),
+                                    _stream(q, stream)), "fa_bwd_ex")
+
+
+def fa_decode_ex(q, k, v, o, lse, scale: float, num_splits: int, workspace, stream=None):
+    """fa_decode with k, v of H_kv heads: q [B,H,1,d], k/v [B,H_kv,Nkv,d]."""
+    torch = _torch()
+    B, H, _, d = q.shape
+    hkv = _kv_heads(q, k)
+    Nkv = k.shape[2]
+    args = [_dev(q, "q", k.dtype, (B, H, 1, d)), _dev(k, "k"), _dev(v, "v", k.dtype, k.shape),
+            _dev(o, "o", k.dtype, (B, H, 1, d)),
+            _dev(lse, "lse", torch.float32, (B, H)) if lse is not None else ctypes.c_void_p(0)]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fa_decode_ex(*args, B, H, hkv, Nkv, d, float(scale), int(num_splits),
+                                       _dev(workspace, "workspace"), nbytes, _dt_code(k),
+                                       _stream(k, stream)), "fa_decode_ex")
+
+
 # ------------------------------------------------------------------ convenience
 def _default_scale(d: int, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def attention_fwd(q, k, v, scale=None, causal=False, stream=None):
-    """Allocate o and lse and run fa_fwd.  Returns (o, lse)."""
+def attention_fwd(q, k, v, scale=None, causal=False, stream=None, window=0):
+    """Allocate o and lse and run fa_fwd (fa_fwd_ex when k, v have fewer heads than q or a
+    window is given).  Returns (o, lse)."""
     torch = _torch()
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, o, lse, _default_scale(d, scale), causal, stream)
+    if k.shape[1] != H or window:
+        fa_fwd_ex(q, k, v, o, lse, _default_scale(d, scale), causal, window, stream)
+    else:
+        fa_fwd(q, k, v, o, lse, _default_scale(d, scale), causal, stream)
     return o, lse
 
 
@@ -180,29 +249,40 @@ def bwd_workspace(q):
     return torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
 
 
-def decode_workspace(k, num_splits: int):
+def decode_workspace(k, num_splits: int, heads=None):
+    """Workspace for fa_decode(_ex); heads = query heads (default: k's heads)."""
     torch = _torch()
     B, H, _, d = k.shape
+    H = H if heads is None else int(heads)
     return torch.empty(fa_decode_workspace_bytes(B, H, d, num_splits), dtype=torch.uint8,
                        device=k.device)
 
 
-def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None):
-    """Allocate gradients (and workspace if not given) and run fa_bwd.  Returns (dq, dk, dv)."""
+def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None,
+                  window=0):
+    """Allocate gradients (and workspace if not given) and run fa_bwd (fa_bwd_ex for grouped
+    heads or a window).  Returns (dq, dk, dv)."""
     torch = _torch()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = bwd_workspace(q) if workspace is None else workspace
-    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, _default_scale(q.shape[-1], scale), causal,
-           stream)
+    sc = _default_scale(q.shape[-1], scale)
+    if k.shape[1] != q.shape[1] or window:
+        fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, ws, sc, causal, window, stream)
+    else:
+        fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, sc, causal, stream)
     return dq, dk, dv
 
 
 def attention_decode(q, k, v, scale=None, num_splits=16, workspace=None, stream=None):
-    """Allocate o, lse (and workspace if not given) and run fa_decode.  Returns (o, lse)."""
+    """Allocate o, lse (and workspace if not given) and run fa_decode (fa_decode_ex when k, v
+    have fewer heads than q).  Returns (o, lse)."""
     torch = _torch()
-    B, H, _, d = k.shape
+    B, H, _, d = q.shape
     o = torch.empty((B, H, 1, d), dtype=k.dtype, device=k.device)
     lse = torch.empty((B, H), dtype=torch.float32, device=k.device)
-    ws = decode_workspace(k, num_splits) if workspace is None else workspace
-    fa_decode(q, k, v, o, lse, _default_scale(d, scale), num_splits, ws, stream)
+    ws = decode_workspace(k, num_splits, heads=H) if workspace is None else workspace
+    if k.shape[1] != H:
+        fa_decode_ex(q, k, v, o, lse, _default_scale(d, scale), num_splits, ws, stream)
+    else:
+        fa_decode(q, k, v, o, lse, _default_scale(d, scale), num_splits, ws, stream)
     return o, lse

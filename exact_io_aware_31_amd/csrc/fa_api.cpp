@@ -35,19 +35,35 @@ fa_status check_common(int B, int H, int N, int d, float scale, fa_dtype dt) {
 
 fa::DType to_dt(fa_dtype dt) { return dt == FA_BF16 ? fa::DType::BF16 : fa::DType::F16; }
 
+// Shared checks of the grouped-head and window arguments.
+fa_status check_ext(int H, int H_kv, int window, int causal) {
+  if (H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
+  if (window < 0) return FA_ERR_SHAPE;
+  if (window > 0 && !causal) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int N, int d, float scale, int causal, fa_dtype dt, void* stream) {
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int H_kv, int N, int d, float scale, int causal, int window,
+                    fa_dtype dt, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  const fa_status st = check_common(B, H, N, d, scale, dt);
+  fa_status st = check_common(B, H, N, d, scale, dt);
   if (st != FA_OK) return st;
+  if ((st = check_ext(H, H_kv, window, causal)) != FA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_ALIGN;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, to_dt(dt)};
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, H_kv, window >= N ? 0 : window, scale, causal != 0,
+                to_dt(dt)};
   return fa::launch_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, fa_dtype dt, void* stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, H, N, d, scale, causal, 0, dt, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -55,21 +71,31 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return fa::bwd_drow_bytes(B, H, N);
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
-                 fa_dtype dt, void* stream) {
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, int B, int H, int H_kv, int N, int d,
+                    float scale, int causal, int window, fa_dtype dt, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-  const fa_status st = check_common(B, H, N, d, scale, dt);
+  fa_status st = check_common(B, H, N, d, scale, dt);
   if (st != FA_OK) return st;
+  if ((st = check_ext(H, H_kv, window, causal)) != FA_OK) return st;
   if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4) || !aligned(workspace, 16))
     return FA_ERR_ALIGN;
   float* drow = static_cast<float*>(workspace);
-  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, drow, B, H, N, d, scale, causal != 0, to_dt(dt)};
+  fa::BwdArgs a{q,     k,    v, o, lse, dout, dq,   dk, dv, drow, B, H, N, d, H_kv,
+                window >= N ? 0 : window, scale, causal != 0, to_dt(dt)};
   return fa::launch_bwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                 fa_dtype dt, void* stream) {
+  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d,
+                   scale, causal, 0, dt, stream);
 }
 
 size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
@@ -77,12 +103,13 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
   return fa::decode_part_o_bytes(B, H, d, num_splits) + fa::decode_part_lse_bytes(B, H, num_splits);
 }
 
-fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                    int Nkv, int d, float scale, int num_splits, void* workspace,
-                    size_t workspace_bytes, fa_dtype dt, void* stream) {
+fa_status fa_decode_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int H_kv, int Nkv, int d, float scale, int num_splits,
+                       void* workspace, size_t workspace_bytes, fa_dtype dt, void* stream) {
   if (!q || !k || !v || !o) return FA_ERR_NULL;
-  const fa_status st = check_common(B, H, Nkv, d, scale, dt);
+  fa_status st = check_common(B, H, Nkv, d, scale, dt);
   if (st != FA_OK) return st;
+  if ((st = check_ext(H, H_kv, 0, 0)) != FA_OK) return st;
   if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
   if ((long long)B * H * num_splits > kMaxGrid) return FA_ERR_SHAPE;
   if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits))
@@ -93,9 +120,17 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              fa::decode_part_o_bytes(B, H, d, num_splits));
-  fa::DecodeArgs a{q, k, v, o, lse, part_o, part_lse, B, H, Nkv, d, num_splits, scale, to_dt(dt)};
+  fa::DecodeArgs a{q, k, v, o, lse, part_o, part_lse, B, H, Nkv, d, num_splits, H_kv, scale,
+                   to_dt(dt)};
   return fa::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK
                                                                                 : FA_ERR_HIP;
+}
+
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                    int Nkv, int d, float scale, int num_splits, void* workspace,
+                    size_t workspace_bytes, fa_dtype dt, void* stream) {
+  return fa_decode_ex(q, k, v, o, lse, B, H, H, Nkv, d, scale, num_splits, workspace,
+                      workspace_bytes, dt, stream);
 }
 
 const char* fa_status_string(fa_status s) {
@@ -105,7 +140,8 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: bad sizes or scale";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: element type must be FA_F16 or FA_BF16";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointer not aligned as required";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128; a window needs causal";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a kernel launch";
     case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits out of range";

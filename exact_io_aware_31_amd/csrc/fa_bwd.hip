@@ -71,12 +71,14 @@ constexpr int KV_WAVES = 4;
 constexpr int KV_BK = 32 * KV_WAVES;  // keys per workgroup
 constexpr int KV_BQ = 32;             // query rows per step
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ drow,
-    T* __restrict__ dK, T* __restrict__ dV, int N, int nkb, int total, float scale, float c) {
+    T* __restrict__ dK, T* __restrict__ dV, int N, int nkb, int total, int group, int window,
+    float scale, float c) {
   using v8 = typename Vec<T>::v8;
+  if constexpr (!WIN) window = 0;  // window code only in the WIN instantiation
   constexpr int BK = KV_BK, BQ = KV_BQ, NB = D / 32;
   constexpr int SPW_Q = BQ * D * 2 / 1024 / KV_WAVES;  // load segments per wave per Q tile
   __shared__ __attribute__((aligned(1024))) T Qs[2][BQ * D];
@@ -88,19 +90,19 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   // Work item: XCD-local heads; causal key blocks heaviest (first) first.
   const int p = blockIdx.x;
   const int w = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
-  const int bh = w / nkb;
+  const int kvbh = w / nkb;  // key/value head (over B x H_kv)
   const int kblk = w % nkb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform_int(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int li = lane & 15, grp = lane >> 4;
-  const size_t hoff = (size_t)bh * N * D;
-  const T* __restrict__ Qh = Q + hoff;
+  // K, V, dK, dV of key/value head kvbh; the query heads of its group are
+  // kvbh * group .. kvbh * group + group - 1, and this block's dK, dV sum
+  // over all of them.
+  const size_t hoff = (size_t)kvbh * N * D;
+  const int qh0 = kvbh * group;
   const T* __restrict__ Kh = K + hoff;
   const T* __restrict__ Vh = V + hoff;
-  const T* __restrict__ dOh = dO + hoff;
-  const float* __restrict__ Lh = LSE + (size_t)bh * N;
-  const float* __restrict__ Dh = drow + (size_t)bh * N;
 
   const int kj0 = kblk * BK;
   const int kw0 = kj0 + 32 * wave;  // first key of this wave
@@ -135,14 +137,30 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   // Q and dO tiles of a step go straight into LDS buffer `buf` (rows past the
   // end clamped to row N-1, their probabilities masked to 0); L and D of the
   // step's rows go through registers.
+  // Steps run over the group's query heads, each over query rows qstart ..
+  // qend - 1: causal blocks start at their first key; with a window, queries
+  // from the block's last key + window on see none of its keys.
+  const int qstart = CAUSAL ? kj0 : 0;
+  const int qend = (CAUSAL && window > 0) ? min(N, kj0 + BK - 1 + window) : N;
+  const int nsh = (qend - qstart + BQ - 1) / BQ;  // steps per query head
+  const int nsteps = group * nsh;
+  // (query head, first row) of a step, advanced step by step (no divisions).
+  auto advance = [&](int& qh, int& q0) {
+    q0 += BQ;
+    if (q0 >= qend) {
+      q0 = qstart;
+      ++qh;
+    }
+  };
   float lpre = 0.f, dpre = 0.f;
-  auto load_step = [&](int qi0, int buf) {
-    load_tile<T, D, BQ, KV_WAVES>(Qh, Qs[buf], qi0, N, wave, lane);
-    load_tile<T, D, BQ, KV_WAVES>(dOh, dOs[buf], qi0, N, wave, lane);
+  auto load_step = [&](int qh, int qi0, int buf) {
+    const size_t qoff = (size_t)qh * N * D;
+    load_tile<T, D, BQ, KV_WAVES>(Q + qoff, Qs[buf], qi0, N, wave, lane);
+    load_tile<T, D, BQ, KV_WAVES>(dO + qoff, dOs[buf], qi0, N, wave, lane);
     if (tid < BQ) {
       const int qrow = qi0 + tid;
-      lpre = (qrow < N) ? Lh[qrow] * 1.4426950408889634f : 0.f;
-      dpre = (qrow < N) ? Dh[qrow] : 0.f;
+      lpre = (qrow < N) ? LSE[(size_t)qh * N + qrow] * 1.4426950408889634f : 0.f;
+      dpre = (qrow < N) ? drow[(size_t)qh * N + qrow] : 0.f;
     }
   };
   auto store_step = [&](int buf) {
@@ -153,16 +171,19 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   };
   static_assert(SPW_Q >= 1, "each wave loads part of every tile");
 
-  const int qstart = CAUSAL ? kj0 : 0;
-  const int nsteps = (N - qstart + BQ - 1) / BQ;
-  load_step(qstart, 0);
+  int ld_h = qh0, ld_q = qstart;  // step being loaded
+  int cu_h = qh0, cu_q = qstart;  // step being computed
+  load_step(ld_h, ld_q, 0);
   store_step(0);
   wait_counts<FA_VMCNT_LGKM0(0)>();  // this wave's direct loads (K tile included) have landed
   __syncthreads();
 
   for (int it = 0; it < nsteps; ++it) {
-    const int qi0 = qstart + it * BQ, buf = it & 1;
-    if (it + 1 < nsteps) load_step(qi0 + BQ, buf ^ 1);  // buffer the previous step read
+    const int qi0 = cu_q, buf = it & 1;
+    if (it + 1 < nsteps) {  // into the buffer the previous step read
+      advance(ld_h, ld_q);
+      load_step(ld_h, ld_q, buf ^ 1);
+    }
 
     // This step's buffer: tiles are 32 D * 2 bytes apart, above every in-tile
     // offset, so adding the buffer offset commutes with the XORs.  The empty
@@ -174,9 +195,12 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     __builtin_amdgcn_iglp_opt(0);
     // Visibility: query qi0 + ql sees key mykey iff ql >= mykey - qi0 (causal),
     // the query exists (ql < N - qi0) and the key exists.
-    const bool need_mask = (CAUSAL && qi0 < kw0 + 31) || (qi0 + BQ > N) || (kw0 + 32 > N);
+    // Window: query qi0 + ql also needs ql < mykey + window - qi0.
+    const bool need_mask = (CAUSAL && qi0 < kw0 + 31) || (qi0 + BQ > N) || (kw0 + 32 > N) ||
+                           (CAUSAL && window > 0 && qi0 + BQ - 1 >= kw0 + window);
     const int lo = CAUSAL ? mykey - qi0 - 4 * hh : -(1 << 30);
-    const int hi = (key_ok ? N - qi0 : 0) - 4 * hh;
+    const int hi = (key_ok ? min(N - qi0, (CAUSAL && window > 0) ? mykey + window - qi0 : N) : 0) -
+                   4 * hh;
 
     // Issue order within the step: both score-shaped products first (S =
     // Q K_w^T and dP = dO V_w^T, keys on the lanes), so the exponentials of P
@@ -257,6 +281,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
       }
 
     if (it + 1 < nsteps) store_step(buf ^ 1);
+    advance(cu_h, cu_q);
     wait_counts<FA_VMCNT_LGKM0(0)>();  // this wave's direct loads have landed
     __syncthreads();
   }
@@ -279,13 +304,14 @@ constexpr int DQ_WAVES = 8;
 constexpr int DQ_BR = 32 * DQ_WAVES;  // query rows per workgroup
 constexpr int DQ_BC = 64;             // keys per tile
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ drow,
-    T* __restrict__ dQ, int N, int nqb, int total, float scale, float c) {
+    T* __restrict__ dQ, int N, int nqb, int total, int group, int window, float scale, float c) {
   using v8 = typename Vec<T>::v8;
   using v4 = typename Vec<T>::v4;
+  if constexpr (!WIN) window = 0;  // window code only in the WIN instantiation
   constexpr int NW = DQ_WAVES, BR = DQ_BR, BC = DQ_BC, NB = D / 32;
   constexpr int SPW = BC * D * 2 / 1024 / NW;  // tile load segments per wave (vmcnt units)
   __shared__ __attribute__((aligned(1024))) T K0[BC * D], K1[BC * D], K2[BC * D];
@@ -301,8 +327,9 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
   const int l32 = lane & 31, hh = lane >> 5;
   const int li = lane & 15, grp = lane >> 4;
   const size_t hoff = (size_t)bh * N * D;
-  const T* __restrict__ Kh = K + hoff;
-  const T* __restrict__ Vh = V + hoff;
+  const size_t kvoff = (size_t)(bh / group) * N * D;  // the group's key/value head
+  const T* __restrict__ Kh = K + kvoff;
+  const T* __restrict__ Vh = V + kvoff;
 
   const int qw0 = qb * BR + 32 * wave;  // first query row of this wave
   const int myq = qw0 + l32;
@@ -326,6 +353,9 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, (qb + 1) * BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
+  // Sliding window: tiles before the block's first visible key are skipped.
+  const int kbase = (CAUSAL && window > 0) ? (max(0, qb * BR - window + 1) / BC) * BC : 0;
+  const int nt = ntiles - kbase / BC;
   // Rows past the end of a tile are clamped to row N-1 and masked.
   auto load_kv = [&](const T* __restrict__ src, T* dst, int kb) {
     load_tile<T, D, BC, NW>(src, dst, kb, N, wave, lane);
@@ -338,11 +368,11 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
   const uint32_t tb = tile_tr_base<D>(4 * hh + (li >> 2), 16 * (grp & 1) + 4 * (li & 3));
 
   // Tiles 0 and 1 in flight; wait for tile 0.
-  load_kv(Kh, K0, 0);
-  load_kv(Vh, V0, 0);
-  if (ntiles > 1) {
-    load_kv(Kh, K1, BC);
-    load_kv(Vh, V1, BC);
+  load_kv(Kh, K0, kbase);
+  load_kv(Vh, V0, kbase);
+  if (nt > 1) {
+    load_kv(Kh, K1, kbase + BC);
+    load_kv(Vh, V1, kbase + BC);
     wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
   } else {
     wait_counts<FA_VMCNT_LGKM0(0)>();
@@ -352,20 +382,23 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
   // One tile: tile j+2 starts loading into the buffer tile j-1 used, tile j is
   // computed, and before the barrier this wave's loads of tile j+1 are done.
   auto tile_step = [&](int j, const T* __restrict__ kt, const T* __restrict__ vt, T* kn, T* vn) {
-    const int kb = j * BC;
-    const bool more = j + 2 < ntiles;
+    const int kb = kbase + j * BC;
+    const bool more = j + 2 < nt;
     if (more) {
       load_kv(Kh, kn, kb + 2 * BC);
       load_kv(Vh, vn, kb + 2 * BC);
     }
-    if (!CAUSAL || kb <= qw0 + 31) {
+    if (!CAUSAL || (kb <= qw0 + 31 && (window == 0 || kb + BC - 1 > qw0 - window))) {
       // Keys past the end and, on diagonal tiles, keys after the query are
       // dropped: key kb + 32 sb + 8 (r / 4) + 4 hh + (r % 4) is kept iff its
       // offset within the tile is <= lim.
-      const bool need_mask = (CAUSAL && kb + BC - 1 > qw0) || (kb + BC > N);
+      const bool need_mask = (CAUSAL && kb + BC - 1 > qw0) || (kb + BC > N) ||
+                             (CAUSAL && window > 0 && kb <= qw0 + 31 - window);
       int lim = N - 1 - kb;
       if (CAUSAL) lim = min(lim, myq - kb);
       lim -= 4 * hh;
+      // Window: keys at tile offset < llim are too old for this row.
+      const int llim = (window > 0 ? myq - window + 1 - kb : -(1 << 30)) - 4 * hh;
       // Opaque copies of the bases keep the XORs per tile instead of hoisted
       // into sixteen loop-invariant registers.
       uint32_t rbs = rb, tbs = tb;
@@ -393,7 +426,8 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
           for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (32 * sb + 8 * (r >> 2) + (r & 3) > lim) s[sb][r] = -INFINITY;
+              if (32 * sb + 8 * (r >> 2) + (r & 3) > lim || 32 * sb + 8 * (r >> 2) + (r & 3) < llim)
+                s[sb][r] = -INFINITY;
         }
         // Per 32 keys: dS^T = P^T o (dP^T - D), then dQ^T += K^T dS^T for
         // those keys (K^T from two transpose reads per MFMA).
@@ -430,10 +464,10 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
     bare_barrier();
   };
   // Unrolled by three so each step names its ring buffers statically.
-  for (int j = 0; j < ntiles; j += 3) {
+  for (int j = 0; j < nt; j += 3) {
     tile_step(j, K0, V0, K2, V2);
-    if (j + 1 < ntiles) tile_step(j + 1, K1, V1, K0, V0);
-    if (j + 2 < ntiles) tile_step(j + 2, K2, V2, K1, V1);
+    if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
+    if (j + 2 < nt) tile_step(j + 2, K2, V2, K1, V1);
   }
 
   // dQ = scale * dQ^T transposed back: lane writes row myq.
@@ -452,7 +486,7 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool WIN>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.H * a.N;
   const long pre_threads = rows * (D / 8);
@@ -466,25 +500,33 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const T* v = static_cast<const T*>(a.v);
   const T* dout = static_cast<const T*>(a.dout);
 
+  const int group = a.H / a.Hkv;
+  const int window = WIN ? a.window : 0;
   const int nkb = (a.N + KV_BK - 1) / KV_BK;
-  const int kv_total = a.B * a.H * nkb;
-  hipLaunchKernelGGL((bwd_kv_kernel<T, D, CAUSAL>), dim3(kv_total), dim3(KV_WAVES * 64), 0, s, q, k,
+  const int kv_total = a.B * a.Hkv * nkb;
+  hipLaunchKernelGGL((bwd_kv_kernel<T, D, CAUSAL, WIN>), dim3(kv_total), dim3(KV_WAVES * 64), 0, s, q, k,
                      v, dout, a.lse, a.drow, static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, nkb,
-                     kv_total, a.scale, c);
+                     kv_total, group, window, a.scale, c);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   const int nqb = (a.N + DQ_BR - 1) / DQ_BR;
   const int dq_total = a.B * a.H * nqb;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(dq_total), dim3(DQ_WAVES * 64), 0, s, q, k,
-                     v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, a.scale, c);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, WIN>), dim3(dq_total), dim3(DQ_WAVES * 64), 0, s, q, k,
+                     v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group, window,
+                     a.scale, c);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
+  if (!a.causal) return launch_bwd_t<T, D, false, false>(a, s);
+  return a.window > 0 ? launch_bwd_t<T, D, true, true>(a, s) : launch_bwd_t<T, D, true, false>(a, s);
 }
 
 template <typename T>
 static hipError_t launch_bwd_dt(const BwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? launch_bwd_t<T, 64, true>(a, s) : launch_bwd_t<T, 64, false>(a, s);
-  return a.causal ? launch_bwd_t<T, 128, true>(a, s) : launch_bwd_t<T, 128, false>(a, s);
+  return a.d == 64 ? launch_bwd_d<T, 64>(a, s) : launch_bwd_d<T, 128>(a, s);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {

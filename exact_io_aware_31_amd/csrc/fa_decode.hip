@@ -72,7 +72,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     float* __restrict__ part_o, float* __restrict__ part_lse, int Nkv, int splits, int chunk,
-    float c) {
+    int group, float c) {
   using v8 = typename Vec<T>::v8;
   constexpr int LPK = D / 8;                 // lanes per key row
   constexpr int KPI = DEC_THREADS / LPK;     // key rows per workgroup step
@@ -93,7 +93,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
     return;
   }
 
-  const size_t hoff = (size_t)bh * Nkv * D;
+  // Query head bh reads key/value head bh / group ("FlashAttention ontleed",
+  // § "Interactie met de KV-cache tijdens inferentie": query heads may share
+  // key/value heads).  The group's heads have the same chunk index and
+  // grid positions that differ by a multiple of `splits`, so they run close
+  // together on one XCD and share the chunk through its L2.
+  const size_t hoff = (size_t)(bh / group) * Nkv * D;
   const T* __restrict__ Kh = K + hoff;
   const T* __restrict__ Vh = V + hoff;
   float qv[8];
@@ -231,7 +236,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const float c = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(BH * a.splits), dim3(DEC_THREADS), 0, s,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), a.part_o, a.part_lse, a.Nkv, a.splits, chunk, c);
+                     static_cast<const T*>(a.v), a.part_o, a.part_lse, a.Nkv, a.splits, chunk,
+                     a.H / a.Hkv, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(BH), dim3(64), 0, s, a.part_o, a.part_lse,

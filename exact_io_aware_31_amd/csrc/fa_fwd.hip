@@ -36,7 +36,14 @@
 //     exponentiated score below 2^8.
 //   * Causal: tiles entirely above the diagonal are never loaded; per
 //     32-row group, tiles entirely above its rows are skipped; only tiles that
-//     cross the diagonal (or the ragged end) are masked element-wise.
+//     cross the diagonal (or the ragged end) are masked element-wise.  A
+//     sliding window ("03. FlashAttention", § "Variantes et extensions") is
+//     the same at the other end: tiles before the block's first window are
+//     never loaded, tiles before a group's windows are skipped, and tiles
+//     crossing a window's lower edge are masked.
+//   * Grouped key/value heads ("FlashAttention ontleed", § "Interactie met
+//     de KV-cache tijdens inferentie"): query head bh reads K/V head
+//     bh / group; nothing else changes.
 //   * Grid: consecutive work items of one head are placed on one XCD (the
 //     hardware deals workgroups round-robin over the 8 XCDs) so the head's
 //     K/V stay in that XCD's L2; causal query blocks run heaviest first.
@@ -59,12 +66,16 @@ constexpr int FWD_BC = 64;
 constexpr float FWD_RESCALE_SLACK = 8.0f;  // log2 units
 
 
-template <typename T, int D, bool CAUSAL, int NW, int QG>
+template <typename T, int D, bool CAUSAL, bool WIN, int NW, int QG>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    T* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, float c) {
+    T* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, int group, int window,
+    float c) {
   using v8 = typename Vec<T>::v8;
   using v4 = typename Vec<T>::v4;
+  // The sliding-window code exists only in the WIN instantiation (window is
+  // then >= 1 and the mask causal); elsewhere it folds away.
+  if constexpr (!WIN) window = 0;
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32 * QG, BC = FWD_BC;
   constexpr int SPW = BC * D * 2 / 1024 / NW;  // tile load segments per wave (vmcnt units)
@@ -84,9 +95,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   const int wave = uniform_int(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const size_t hoff = (size_t)bh * N * D;
+  // Query head bh reads key/value head bh / group (groups of consecutive
+  // query heads share one; group = 1 is plain multi-head attention).
+  const size_t kvoff = (size_t)(bh / group) * N * D;
   const T* __restrict__ Qh = Q + hoff;
-  const T* __restrict__ Kh = K + hoff;
-  const T* __restrict__ Vh = V + hoff;
+  const T* __restrict__ Kh = K + kvoff;
+  const T* __restrict__ Vh = V + kvoff;
 
   const int qw0 = qb * BR + wave * 32 * QG;  // first query row of this wave
   int myq[QG];
@@ -113,6 +127,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
 
   const int kv_end = CAUSAL ? min(N, (qb + 1) * BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
+  // With a sliding window the block's first visible key is qb BR - window + 1:
+  // tiles before the one holding it are never loaded.
+  const int kbase = (CAUSAL && window > 0) ? (max(0, qb * BR - window + 1) / BC) * BC : 0;
+  const int nt = ntiles - kbase / BC;  // tiles this workgroup streams
 
   // Tile loads (see load_tile): rows past the end are clamped to row N-1;
   // those keys are masked to -inf before the softmax, so their probabilities
@@ -138,11 +156,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
       voff[t][nb] = tile_off<D>(8 * t + 4 * hh + (li >> 2), 32 * nb + 16 * (grp & 1) + 4 * (li & 3));
 
   // Tiles 0 and 1 in flight; wait for tile 0 (vmcnt counts this wave's loads).
-  load_kv(Kh, K0, 0);
-  load_kv(Vh, V0, 0);
-  if (ntiles > 1) {
-    load_kv(Kh, K1, BC);
-    load_kv(Vh, V1, BC);
+  load_kv(Kh, K0, kbase);
+  load_kv(Vh, V0, kbase);
+  if (nt > 1) {
+    load_kv(Kh, K1, kbase + BC);
+    load_kv(Vh, V1, kbase + BC);
     wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
   } else {
     wait_counts<FA_VMCNT_LGKM0(0)>();
@@ -154,8 +172,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   // One tile: tile j+2 starts loading into the buffer tile j-1 used, tile j is
   // computed, and before the barrier this wave's loads of tile j+1 are done.
   auto tile_step = [&](int j, const T* __restrict__ kt, const T* __restrict__ vt, T* kn, T* vn) {
-    const int kb = j * BC;
-    const bool more = j + 2 < ntiles;
+    const int kb = kbase + j * BC;
+    const bool more = j + 2 < nt;
     if (more) {
       load_kv(Kh, kn, kb + 2 * BC);
       load_kv(Vh, vn, kb + 2 * BC);
@@ -164,7 +182,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     bool any_active = false;
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
-      active[g] = !CAUSAL || kb <= qw0 + 32 * g + 31;
+      // Causal: tiles wholly after the group's last row, or (window) wholly
+      // before its first row's window, are skipped.
+      active[g] = !CAUSAL || (kb <= qw0 + 32 * g + 31 &&
+                              (window == 0 || kb + BC - 1 > qw0 + 32 * g - window));
       any_active |= active[g];
     }
     if (any_active) {
@@ -218,16 +239,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
         // Mask keys past the end and, on diagonal tiles, keys after the query:
         // key kb + 32 sb + 8 (r / 4) + 4 hh + (r % 4) is kept iff its offset
         // within the tile is <= lim (a per-lane bound, so 2 VALU ops per score).
-        const bool need_mask = (CAUSAL && kb + BC - 1 > qw0 + 32 * g) || (kb + BC > N);
+        const bool need_mask = (CAUSAL && kb + BC - 1 > qw0 + 32 * g) || (kb + BC > N) ||
+                               (CAUSAL && window > 0 && kb <= qw0 + 32 * g + 31 - window);
         if (need_mask) {
           int lim = N - 1 - kb;
           if (CAUSAL) lim = min(lim, myq[g] - kb);
           lim -= 4 * hh;
+          // Window: keys at tile offset < llim are too old for this row.
+          const int llim = (window > 0 ? myq[g] - window + 1 - kb : -(1 << 30)) - 4 * hh;
 #pragma unroll
           for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (32 * sb + 8 * (r >> 2) + (r & 3) > lim) sacc[g][sb][r] = -INFINITY;
+              if (32 * sb + 8 * (r >> 2) + (r & 3) > lim || 32 * sb + 8 * (r >> 2) + (r & 3) < llim)
+                sacc[g][sb][r] = -INFINITY;
         }
         // Tile row max (3-input max tree), shared by the two halves of the wave.
         float mx = -INFINITY;
@@ -247,7 +272,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
           for (int nb = 0; nb < D / 32; ++nb) oacc[g][nb] *= alpha;
           m_run[g] = m_new;
         }
-        const float mref = m_run[g];
+        // A row whose keys so far are all masked (a window can hide a whole
+        // tile from one row of an active group) still has m = -inf: any
+        // finite reference gives its -inf scores probability 0, not NaN.
+        const float mref = (m_run[g] == -INFINITY) ? 0.f : m_run[g];
         float rs[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial row sums
 #pragma unroll
         for (int sb = 0; sb < BC / 32; ++sb)
@@ -287,10 +315,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     bare_barrier();
   };
   // Unrolled by three so each step names its ring buffers statically.
-  for (int j = 0; j < ntiles; j += 3) {
+  for (int j = 0; j < nt; j += 3) {
     tile_step(j, K0, V0, K2, V2);
-    if (j + 1 < ntiles) tile_step(j + 1, K1, V1, K0, V0);
-    if (j + 2 < ntiles) tile_step(j + 2, K2, V2, K1, V1);
+    if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
+    if (j + 2 < nt) tile_step(j + 2, K2, V2, K1, V1);
   }
 
   // Epilogue: O = O / l, lse = (m + log2 l) ln 2.
@@ -314,21 +342,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool WIN>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const int nqb = (a.N + FWD_BR - 1) / FWD_BR;
   const int total = a.B * a.H * nqb;
   const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, FWD_NW, FWD_QG>), dim3(total), dim3(FWD_NW * 64), 0,
-                     s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.N, nqb, total, c);
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, WIN, FWD_NW, FWD_QG>), dim3(total), dim3(FWD_NW * 64),
+                     0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.N, nqb, total,
+                     a.H / a.Hkv, WIN ? a.window : 0, c);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t s) {
+  if (!a.causal) return launch_fwd_t<T, D, false, false>(a, s);
+  return a.window > 0 ? launch_fwd_t<T, D, true, true>(a, s) : launch_fwd_t<T, D, true, false>(a, s);
 }
 
 template <typename T>
 static hipError_t launch_fwd_dt(const FwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? launch_fwd_t<T, 64, true>(a, s) : launch_fwd_t<T, 64, false>(a, s);
-  return a.causal ? launch_fwd_t<T, 128, true>(a, s) : launch_fwd_t<T, 128, false>(a, s);
+  return a.d == 64 ? launch_fwd_d<T, 64>(a, s) : launch_fwd_d<T, 128>(a, s);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {

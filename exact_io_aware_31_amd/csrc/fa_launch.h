@@ -13,6 +13,8 @@ struct FwdArgs {
   const void* q; const void* k; const void* v;
   void* o; float* lse;
   int B, H, N, d;
+  int Hkv;         // key/value heads; H is a multiple of Hkv
+  int window;      // 0 = none; else (causal) key j visible to query i iff i - window < j <= i
   float scale;
   bool causal;
   DType dt;
@@ -24,6 +26,8 @@ struct BwdArgs {
   void* dq; void* dk; void* dv;
   float* drow;     // [B,H,N] float32 workspace
   int B, H, N, d;
+  int Hkv;         // key/value heads (k, v, dk, dv are [B,Hkv,N,d])
+  int window;      // as in FwdArgs
   float scale;
   bool causal;
   DType dt;
@@ -35,6 +39,7 @@ struct DecodeArgs {
   float* part_o;            // [B,H,S,d] float32 workspace
   float* part_lse;          // [B,H,S] float32 workspace
   int B, H, Nkv, d, splits;
+  int Hkv;                  // key/value heads (k, v are [B,Hkv,Nkv,d])
   float scale;
   DType dt;
 };

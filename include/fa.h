@@ -60,7 +60,7 @@ typedef enum fa_status {
   FA_ERR_SHAPE = 2,       /* B, H, N, Nkv < 1, sizes overflow, or bad scale */
   FA_ERR_DTYPE = 3,       /* dt is not FA_F16 or FA_BF16 */
   FA_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
-  FA_ERR_UNSUPPORTED = 5, /* head dimension other than 64 or 128 */
+  FA_ERR_UNSUPPORTED = 5, /* head dimension other than 64 or 128; window without causal */
   FA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the query says */
   FA_ERR_HIP = 7,         /* the HIP runtime refused a launch */
   FA_ERR_SPLITS = 8       /* num_splits < 1 or above FA_MAX_SPLITS */
@@ -125,6 +125,42 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
 fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int Nkv, int d, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, fa_dtype dt, void* stream);
+
+/*
+ * Grouped key/value heads and a causal sliding window.
+ *
+ * Several query heads may share one key/value head ("FlashAttention ontleed",
+ * § "Interactie met de KV-cache tijdens inferentie"), and the keys a query
+ * sees may be restricted to a window of the most recent ones ("03.
+ * FlashAttention", § "Variantes et extensions": the sliding-window variant
+ * tiles only the keys inside the window).  fa_fwd, fa_bwd and fa_decode are
+ * these calls with H_kv = H and window = 0.
+ *   q, o, dq, dout : [B, H,    N, d]   (decode: [B, H, 1, d])
+ *   k, v, dk, dv   : [B, H_kv, N, d]   (decode: [B, H_kv, Nkv, d])
+ *   H_kv           : key/value heads, >= 1, dividing H.  Query head h reads
+ *                    key/value head h / (H / H_kv) (contiguous groups); dk and
+ *                    dv hold the sum over each group's query heads.
+ *   window         : 0 for no window.  window = w >= 1 requires causal != 0
+ *                    (FA_ERR_UNSUPPORTED otherwise): key j is visible to
+ *                    query i iff i - w < j <= i, i.e. the w most recent keys,
+ *                    the query's own position included.  w >= N is the same
+ *                    as no window.  window < 0 is FA_ERR_SHAPE.
+ *   H_kv < 1 or H not a multiple of H_kv is FA_ERR_SHAPE.
+ * Workspace sizes are those of fa_bwd_workspace_bytes(B, H, N, d) and
+ * fa_decode_workspace_bytes(B, H, d, num_splits), with H the query heads.
+ * Every other convention (dtypes, alignment, lse, ownership, errors,
+ * streams, determinism) is that of fa_fwd / fa_bwd / fa_decode.
+ */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int H_kv, int N, int d, float scale, int causal, int window,
+                    fa_dtype dt, void* stream);
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, int B, int H, int H_kv, int N,
+                    int d, float scale, int causal, int window, fa_dtype dt, void* stream);
+fa_status fa_decode_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int H_kv, int Nkv, int d, float scale, int num_splits,
+                       void* workspace, size_t workspace_bytes, fa_dtype dt, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status s);

@@ -69,14 +69,15 @@ def _draw(gen: torch.Generator, shape, dtype, device, mult: float = 1.0) -> torc
 
 def attention_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
                      device="cpu", q_mult: float = 1.0, with_dout: bool = False,
-                     Nkv: Optional[int] = None):
-    """Q [B,H,N,d], K and V [B,H,Nkv or N,d] (and dO like Q) drawn in that order."""
+                     Nkv: Optional[int] = None, Hkv: Optional[int] = None):
+    """Q [B,H,N,d], K and V [B,Hkv or H,Nkv or N,d] (and dO like Q) drawn in that order."""
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     nk = N if Nkv is None else Nkv
+    hk = H if Hkv is None else Hkv
     q = _draw(gen, (B, H, N, d), dtype, device, q_mult)
-    k = _draw(gen, (B, H, nk, d), dtype, device)
-    v = _draw(gen, (B, H, nk, d), dtype, device)
+    k = _draw(gen, (B, hk, nk, d), dtype, device)
+    v = _draw(gen, (B, hk, nk, d), dtype, device)
     if not with_dout:
         return q, k, v
     do = _draw(gen, (B, H, N, d), dtype, device)

@@ -35,8 +35,9 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_decode", "fa_bwd_workspace_bytes",
-                          "fa_decode_workspace_bytes", "fa_status_string", "fa_version"}
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_decode", "fa_fwd_ex", "fa_bwd_ex",
+                          "fa_decode_ex", "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes",
+                          "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/fa.h but not exported"
 
@@ -120,6 +121,51 @@ def test_decode_validation(lib):
     assert dec(lib, ws_bytes=need - 4) == ERR["FA_ERR_WORKSPACE"]
     assert dec(lib, k=P_ODD) == ERR["FA_ERR_ALIGN"]
     assert dec(lib, lse=P_ODD) == ERR["FA_ERR_ALIGN"]
+
+
+def fwd_ex(lib, B=1, H=4, H_kv=2, N=16, d=64, causal=1, window=0, **ptrs):
+    p = dict(q=P, k=P, v=P, o=P, lse=P)
+    p.update(ptrs)
+    return lib.fa_fwd_ex(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, H_kv, N, d, 0.125,
+                         causal, window, 1, NULL)
+
+
+def bwd_ex(lib, B=1, H=4, H_kv=2, N=16, d=64, causal=1, window=0, ws_bytes=1 << 30, **ptrs):
+    p = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, ws=P)
+    p.update(ptrs)
+    return lib.fa_bwd_ex(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"],
+                         p["dv"], p["ws"], ws_bytes, B, H, H_kv, N, d, 0.125, causal, window, 0,
+                         NULL)
+
+
+def dec_ex(lib, B=2, H=8, H_kv=2, Nkv=100, d=128, splits=4, ws_bytes=1 << 30, **ptrs):
+    p = dict(q=P, k=P, v=P, o=P, lse=P, ws=P)
+    p.update(ptrs)
+    return lib.fa_decode_ex(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, H_kv, Nkv, d, 0.1,
+                            splits, p["ws"], ws_bytes, 1, NULL)
+
+
+@pytest.mark.parametrize("call", [fwd_ex, bwd_ex, dec_ex], ids=["fwd_ex", "bwd_ex", "decode_ex"])
+def test_grouped_head_validation(lib, call):
+    for h_kv in (0, -2, 3, 5):  # 4 (or 8) query heads: not a divisor
+        assert call(lib, H_kv=h_kv) == ERR["FA_ERR_SHAPE"]
+    assert call(lib, q=NULL) == ERR["FA_ERR_NULL"]
+    assert call(lib, k=P_ODD) == ERR["FA_ERR_ALIGN"]
+
+
+@pytest.mark.parametrize("call", [fwd_ex, bwd_ex], ids=["fwd_ex", "bwd_ex"])
+def test_window_validation(lib, call):
+    assert call(lib, window=-1) == ERR["FA_ERR_SHAPE"]
+    assert call(lib, window=4, causal=0) == ERR["FA_ERR_UNSUPPORTED"]
+    assert call(lib, d=96, window=4) == ERR["FA_ERR_UNSUPPORTED"]
+
+
+def test_bwd_ex_workspace_is_per_query_head(lib):
+    need = fa.fa_bwd_workspace_bytes(1, 4, 16, 64)
+    assert bwd_ex(lib, ws=NULL) == ERR["FA_ERR_WORKSPACE"]
+    assert bwd_ex(lib, ws_bytes=need - 1) == ERR["FA_ERR_WORKSPACE"]
+    need = fa.fa_decode_workspace_bytes(2, 8, 128, 4)
+    assert dec_ex(lib, ws_bytes=need - 4) == ERR["FA_ERR_WORKSPACE"]
 
 
 def test_binding_rejects_host_tensors():
