@@ -13,9 +13,18 @@ HIP events recorded on the stream its kernels run on (torch's current
 stream, which the binding hands to the library).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--only fwd|bwd|decode]
+                       [--only fwd|bwd|decode|ext]
 --only runs a single entry point per step (for per-kernel profiling); the
-JSON line then carries only that entry's figures.
+JSON line then carries only that entry's figures.  --only ext runs only the
+extension workloads.
+
+After the timed steps, the extension entry points are timed on their own
+workloads, outside the step (they do not enter value or ms_per_step):
+  * fa_decode_ex, grouped key/value heads: B=64 H=32 H_kv=8 Nkv=16384 d=128
+    bf16, 16 chunks; GB/s of algorithmic bytes, K and V counted once per
+    key/value head;
+  * fa_fwd_ex, causal sliding window of 1024 keys: B=1 H=32 N=8192 d=128
+    bf16; TFLOP/s of useful work, 4 d FLOPs per visible (query, key) pair.
 --copy-calibration BYTES only copies a BYTES-sized device buffer 5 times
 (a plain copy kernel of known traffic, used to scale HBM byte counters).
 """
@@ -82,6 +91,51 @@ def cpu_baseline(q, k, v, do, lse_unused, decode_inputs, heads: int, scale: floa
                       f"N={n} d={d} causal workload ({secs:.1f} s; useful-FLOP formula)"}
 
 
+def time_calls(torch, call, reps: int, warmup: int = 2) -> float:
+    """Average ms per call, HIP events on the current stream (the one the binding uses)."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def measure_extensions(fa, torch, dev, reps: int):
+    """Grouped-head decode and sliding-window forward on their own workloads."""
+    from synth_inputs import GQA_DECODE_16K, WINDOW_FWD_8K, workload_inputs
+    out = []
+    w = WINDOW_FWD_8K
+    q, k, v = workload_inputs(w, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ms = time_calls(torch, lambda: fa.fa_fwd_ex(q, k, v, o, lse, w.scale, True, w.window), reps)
+    pairs = w.window * (w.window + 1) // 2 + (w.N - w.window) * w.window
+    tf = 4 * w.B * w.H * w.d * pairs / (ms * 1e-3) / 1e12
+    out.append({"workload": w.name, "entry": "fa_fwd_ex", "bound": "mfma",
+                "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / PEAK_BF16_TFLOPS, 4), "ms": round(ms, 4)})
+    del q, k, v, o, lse
+    w = GQA_DECODE_16K
+    q, k, v = workload_inputs(w, dev)
+    o = torch.empty((w.B, w.H, 1, w.d), dtype=w.dtype, device=dev)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    ws = fa.decode_workspace(k, w.splits, heads=w.H)
+    ms = time_calls(torch, lambda: fa.fa_decode_ex(q, k, v, o, lse, w.scale, w.splits, ws), reps)
+    nbytes = (2 * w.B * w.Hkv * w.Nkv * w.d + 2 * w.B * w.H * w.d) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out.append({"workload": w.name, "entry": "fa_decode_ex", "bound": "hbm",
+                "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4)})
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(torch, nbytes: int, reps: int = 5):
     """Time a plain device-to-device copy of nbytes (reads nbytes, writes nbytes)."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
@@ -108,7 +162,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2)
-    ap.add_argument("--only", choices=("fwd", "bwd", "decode"), default=None)
+    ap.add_argument("--only", choices=("fwd", "bwd", "decode", "ext"), default=None)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -130,6 +184,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w, wd = FWD_8K, DECODE_16K
+    if args.only == "ext":
+        ext = measure_extensions(fa, torch, dev, args.steps)
+        print(json.dumps({"metric": "extension entry points (grouped-head decode GB/s, "
+                                    "sliding-window forward TFLOP/s)",
+                          "value": ext[1]["achieved"], "unit": "GB/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": 2, "higher_is_better": True,
+                          "data": "synthetic", "extensions": ext, "only": "ext"}), flush=True)
+        return
 
     # Inputs drawn on the GPU and resident in HBM before timing starts.
     q, k, v, do = attention_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, dev, q_mult=w.q_mult,
@@ -229,6 +291,8 @@ def main():
         "rooflines": roofs,
         "wall_s_timed": round(t_wall, 3),
     }
+    if args.only is None:
+        out["extensions"] = measure_extensions(fa, torch, dev, max(5, args.steps // 2))
     if args.only is not None:
         out["only"] = args.only
     if not args.no_cpu_baseline and args.only is None:

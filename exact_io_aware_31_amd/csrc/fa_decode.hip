@@ -67,8 +67,14 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Kernel 1: one workgroup per (head, chunk).
-template <typename T, int D>
+// Kernel 1: one workgroup per (G query heads, chunk).  The G heads share one
+// key/value head ("FlashAttention ontleed", § "Interactie met de KV-cache
+// tijdens inferentie": query heads may share key/value heads), so the chunk
+// of K and V is read once for all of them: each key row is dotted with G
+// queries and each value row accumulated into G outputs.  G = 1 is plain
+// multi-head decode.  Query heads h0 .. h0 + G - 1 (over B x H) with
+// h0 = kvbh * group + G * (workgroup index within the group).
+template <typename T, int D, int G>
 __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     float* __restrict__ part_o, float* __restrict__ part_lse, int Nkv, int splits, int chunk,
@@ -76,42 +82,53 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
   using v8 = typename Vec<T>::v8;
   constexpr int LPK = D / 8;                 // lanes per key row
   constexpr int KPI = DEC_THREADS / LPK;     // key rows per workgroup step
-  __shared__ float sc[DEC_SUB];
-  __shared__ float red[DEC_THREADS / 64];
+  constexpr int NWV = DEC_THREADS / 64;      // waves
+  __shared__ float sc[G][DEC_SUB];
+  __shared__ float red[G][NWV];
   __shared__ float oacc_s[KPI][D + 4];
 
-  const int bh = blockIdx.x / splits, split = blockIdx.x % splits;
+  const int wg = blockIdx.x / splits, split = blockIdx.x % splits;
+  const int per_kv = group / G;                      // workgroups per key/value head
+  const int kvbh = wg / per_kv;                      // key/value head (over B x H_kv)
+  const int h0 = kvbh * group + G * (wg % per_kv);   // first query head (over B x H)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = tid / LPK, col = tid % LPK;
   const int k_lo = split * chunk;
   const int k_hi = min(Nkv, k_lo + chunk);
-  float* __restrict__ po = part_o + ((size_t)bh * splits + split) * D;
 
   if (k_lo >= k_hi) {  // empty chunk: weight zero in the merge
-    for (int i = tid; i < D; i += DEC_THREADS) po[i] = 0.f;
-    if (tid == 0) part_lse[(size_t)bh * splits + split] = -INFINITY;
+#pragma unroll
+    for (int gh = 0; gh < G; ++gh) {
+      float* __restrict__ po = part_o + ((size_t)(h0 + gh) * splits + split) * D;
+      for (int i = tid; i < D; i += DEC_THREADS) po[i] = 0.f;
+      if (tid == 0) part_lse[(size_t)(h0 + gh) * splits + split] = -INFINITY;
+    }
     return;
   }
 
-  // Query head bh reads key/value head bh / group ("FlashAttention ontleed",
-  // § "Interactie met de KV-cache tijdens inferentie": query heads may share
-  // key/value heads).  The group's heads have the same chunk index and
-  // grid positions that differ by a multiple of `splits`, so they run close
-  // together on one XCD and share the chunk through its L2.
-  const size_t hoff = (size_t)(bh / group) * Nkv * D;
+  const size_t hoff = (size_t)kvbh * Nkv * D;
   const T* __restrict__ Kh = K + hoff;
   const T* __restrict__ Vh = V + hoff;
-  float qv[8];
-  widen8<T>(ld16<v8>(Q + (size_t)bh * D + 8 * col), qv);
+  float qv[G][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) qv[i] *= c;  // scores come out in log2 units
+  for (int gh = 0; gh < G; ++gh) {
+    widen8<T>(ld16<v8>(Q + (size_t)(h0 + gh) * D + 8 * col), qv[gh]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[gh][i] *= c;  // scores come out in log2 units
+  }
 
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float o[G][8], m_run[G], l_run[G];
+#pragma unroll
+  for (int gh = 0; gh < G; ++gh) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[gh][i] = 0.f;
+    m_run[gh] = -INFINITY;
+    l_run[gh] = 0.f;
+  }
 
   for (int s0 = k_lo; s0 < k_hi; s0 += DEC_SUB) {
     const int s1 = min(k_hi, s0 + DEC_SUB);
-    // K pass: scores of keys s0..s1-1 into LDS.
+    // K pass: scores of keys s0..s1-1 for the G heads into LDS.
     for (int kk = s0 + slot; kk < s1; kk += KPI * DEC_UNROLL) {
       // Rows past the sub-chunk are clamped to its last row (always valid);
       // their scores are never stored.
@@ -125,45 +142,62 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
       for (int u = 0; u < DEC_UNROLL; ++u) {
         float kf[8];
         widen8<T>(kr[u], kf);
-        float dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(qv[i], kf[i], dot);
-        dot = row_sum<LPK>(dot);
         const int key = kk + u * KPI;
-        if (col == 0 && key < s1) sc[key - s0] = dot;
+#pragma unroll
+        for (int gh = 0; gh < G; ++gh) {
+          float dot = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(qv[gh][i], kf[i], dot);
+          dot = row_sum<LPK>(dot);
+          if (col == 0 && key < s1) sc[gh][key - s0] = dot;
+        }
       }
     }
     __syncthreads();
-    // Chunk maximum.
-    float mx = -INFINITY;
-    for (int i = tid; i < s1 - s0; i += DEC_THREADS) mx = fmaxf(mx, sc[i]);
-    mx = wave_max(mx);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    mx = red[0];
+    // Chunk maxima, one per head.
+    float mx[G];
 #pragma unroll
-    for (int wv = 1; wv < DEC_THREADS / 64; ++wv) mx = fmaxf(mx, red[wv]);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    __syncthreads();  // everyone has read red[]
-    // Probabilities (unnormalised) in place, and their sum.
-    float ps = 0.f;
-    for (int i = tid; i < s1 - s0; i += DEC_THREADS) {
-      const float pe = fast_exp2(sc[i] - m_new);
-      sc[i] = pe;
-      ps += pe;
+    for (int gh = 0; gh < G; ++gh) {
+      mx[gh] = -INFINITY;
+      for (int i = tid; i < s1 - s0; i += DEC_THREADS) mx[gh] = fmaxf(mx[gh], sc[gh][i]);
+      mx[gh] = wave_max(mx[gh]);
+      if (lane == 0) red[gh][wave] = mx[gh];
     }
-    ps = wave_sum(ps);
-    if (lane == 0) red[wave] = ps;
     __syncthreads();
-    ps = 0.f;
+    float alpha[G], m_new[G];
 #pragma unroll
-    for (int wv = 0; wv < DEC_THREADS / 64; ++wv) ps += red[wv];
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
+    for (int gh = 0; gh < G; ++gh) {
+      float m = red[gh][0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= alpha;
-    // V pass: o += p * v over this lane's key rows.
+      for (int wv = 1; wv < NWV; ++wv) m = fmaxf(m, red[gh][wv]);
+      m_new[gh] = fmaxf(m_run[gh], m);
+      alpha[gh] = fast_exp2(m_run[gh] - m_new[gh]);
+    }
+    __syncthreads();  // everyone has read red[]
+    // Probabilities (unnormalised) in place, and their sums.
+#pragma unroll
+    for (int gh = 0; gh < G; ++gh) {
+      float ps = 0.f;
+      for (int i = tid; i < s1 - s0; i += DEC_THREADS) {
+        const float pe = fast_exp2(sc[gh][i] - m_new[gh]);
+        sc[gh][i] = pe;
+        ps += pe;
+      }
+      ps = wave_sum(ps);
+      if (lane == 0) red[gh][wave] = ps;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int gh = 0; gh < G; ++gh) {
+      float ps = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < NWV; ++wv) ps += red[gh][wv];
+      l_run[gh] = l_run[gh] * alpha[gh] + ps;
+      m_run[gh] = m_new[gh];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[gh][i] *= alpha[gh];
+    }
+    // V pass: o += p * v over this lane's key rows, for every head.
     for (int kk = s0 + slot; kk < s1; kk += KPI * DEC_UNROLL) {
       // Clamped rows as in the K pass; they get weight 0 below.
       v8 vr[DEC_UNROLL];
@@ -175,29 +209,38 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
 #pragma unroll
       for (int u = 0; u < DEC_UNROLL; ++u) {
         const int key = kk + u * KPI;
-        const float pe = (key < s1) ? sc[key - s0] : 0.f;
         float vf[8];
         widen8<T>(vr[u], vf);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = __builtin_fmaf(pe, vf[i], o[i]);
+        for (int gh = 0; gh < G; ++gh) {
+          const float pe = (key < s1) ? sc[gh][key - s0] : 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[gh][i] = __builtin_fmaf(pe, vf[i], o[gh][i]);
+        }
       }
     }
     __syncthreads();  // sc[] and red[] are reused by the next sub-chunk
   }
 
-  // Sum the per-slot partial outputs, normalise, write the chunk summary.
+  // Per head: sum the per-slot partial outputs, normalise, write the chunk summary.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) oacc_s[slot][8 * col + i] = o[i];
-  __syncthreads();
-  const float inv = 1.f / l_run;
-  for (int x = tid; x < D; x += DEC_THREADS) {
-    float s = 0.f;
+  for (int gh = 0; gh < G; ++gh) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) oacc_s[slot][8 * col + i] = o[gh][i];
+    __syncthreads();
+    float* __restrict__ po = part_o + ((size_t)(h0 + gh) * splits + split) * D;
+    const float inv = 1.f / l_run[gh];
+    for (int x = tid; x < D; x += DEC_THREADS) {
+      float sum = 0.f;
 #pragma unroll 4
-    for (int sl = 0; sl < KPI; ++sl) s += oacc_s[sl][x];
-    po[x] = s * inv;
+      for (int sl = 0; sl < KPI; ++sl) sum += oacc_s[sl][x];
+      po[x] = sum * inv;
+    }
+    if (tid == 0)
+      part_lse[(size_t)(h0 + gh) * splits + split] =
+          (m_run[gh] + log2f(l_run[gh])) * 0.69314718055994531f;
+    __syncthreads();  // oacc_s is reused by the next head
   }
-  if (tid == 0)
-    part_lse[(size_t)bh * splits + split] = (m_run + log2f(l_run)) * 0.69314718055994531f;
 }
 
 // Kernel 2: one wave per head merges its chunk summaries.
@@ -229,19 +272,29 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   if (LSE && lane == 0) LSE[bh] = big + logf(wsum);
 }
 
-template <typename T, int D>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-  const int BH = a.B * a.H;
+template <typename T, int D, int G>
+static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
   const int chunk = (a.Nkv + a.splits - 1) / a.splits;
   const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(BH * a.splits), dim3(DEC_THREADS), 0, s,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), a.part_o, a.part_lse, a.Nkv, a.splits, chunk,
-                     a.H / a.Hkv, c);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(a.B * a.H / G * a.splits),
+                     dim3(DEC_THREADS), 0, s, static_cast<const T*>(a.q),
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.part_o, a.part_lse,
+                     a.Nkv, a.splits, chunk, a.H / a.Hkv, c);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+  // Query heads per workgroup: the largest of 4, 2, 1 dividing the group.
+  // (Eight heads need more than 256 registers per lane: one wave per SIMD,
+  // too few loads in flight for the HBM stream.)
+  const int group = a.H / a.Hkv;
+  hipError_t e = (group % 4 == 0)   ? launch_decode_g<T, D, 4>(a, s)
+                 : (group % 2 == 0) ? launch_decode_g<T, D, 2>(a, s)
+                                    : launch_decode_g<T, D, 1>(a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(BH), dim3(64), 0, s, a.part_o, a.part_lse,
-                     static_cast<T*>(a.o), a.lse, a.splits);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.B * a.H), dim3(64), 0, s, a.part_o,
+                     a.part_lse, static_cast<T*>(a.o), a.lse, a.splits);
   return hipGetLastError();
 }
 

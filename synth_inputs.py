@@ -33,6 +33,8 @@ class Workload:
     q_mult: float = 1.0  # exact power-of-two factor applied to Q
     Nkv: int = 0         # key/value length for decode
     splits: int = 0      # history chunks per head for decode
+    Hkv: int = 0         # key/value heads (0: as many as query heads)
+    window: int = 0      # causal sliding window (0: none)
     note: str = field(default="", compare=False)
 
     @property
@@ -52,7 +54,16 @@ BWD_4K = Workload("bwd_b2h16n4096d128_bf16_causal", "bwd", 2, 16, 4096, 128, tor
 DECODE_16K = Workload("decode_b64h32kv16384d128_bf16_s16", "decode", 64, 32, 1, 128,
                       torch.bfloat16, False, 1005, Nkv=16384, splits=16)
 
-WORKLOADS = {w.name: w for w in (TINY_FWD, FWD_2K, FWD_8K, BWD_4K, DECODE_16K)}
+# Grouped key/value heads and a sliding window on the same shapes.
+GQA_DECODE_16K = Workload("decode_b64h32kv8_kv16384d128_bf16_s16", "decode", 64, 32, 1, 128,
+                          torch.bfloat16, False, 1006, Nkv=16384, splits=16, Hkv=8,
+                          note="4 query heads per key/value head")
+WINDOW_FWD_8K = Workload("fwd_b1h32n8192d128_bf16_window1024", "fwd", 1, 32, 8192, 128,
+                         torch.bfloat16, True, 1007, window=1024,
+                         note="causal sliding window of 1024 keys")
+
+WORKLOADS = {w.name: w for w in (TINY_FWD, FWD_2K, FWD_8K, BWD_4K, DECODE_16K, GQA_DECODE_16K,
+                                 WINDOW_FWD_8K)}
 
 
 def _draw(gen: torch.Generator, shape, dtype, device, mult: float = 1.0) -> torch.Tensor:
@@ -86,8 +97,9 @@ def attention_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: i
 
 def workload_inputs(w: Workload, device="cpu"):
     """Inputs of a named workload (decode: q is [B,H,1,d])."""
+    hkv = w.Hkv or None
     if w.kind == "decode":
         return attention_inputs(w.B, w.H, 1, w.d, w.dtype, w.seed, device, w.q_mult,
-                                Nkv=w.Nkv)
+                                Nkv=w.Nkv, Hkv=hkv)
     return attention_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, device, w.q_mult,
-                            with_dout=(w.kind == "bwd"))
+                            with_dout=(w.kind == "bwd"), Hkv=hkv)
