@@ -16,6 +16,12 @@ Low-level functions carry the C names and take caller-allocated tensors:
     fa_status_string(code), fa_version()
 Convenience wrappers allocate outputs and workspaces with torch:
     attention_fwd, attention_bwd, attention_decode
+and attention(q, k, v, scale=None, causal=False, window=0) is a differentiable
+drop-in for torch's scaled_dot_product_attention on [B, H, N, d] fp16/bf16
+device tensors (the PyTorch entry point the pages name: "FlashAttention
+ontleed", § "Praktische integratie en hardware-eisen"; "03. FlashAttention",
+§ "Intégration en pratique"): its forward saves O and the log-sum-exp and its
+backward recomputes P through fa_bwd ("03. FlashAttention", § "Backward pass").
 """
 import ctypes
 import math
@@ -286,3 +292,48 @@ def attention_decode(q, k, v, scale=None, num_splits=16, workspace=None, stream=
     else:
         fa_decode(q, k, v, o, lse, _default_scale(d, scale), num_splits, ws, stream)
     return o, lse
+
+
+# ------------------------------------------------------------------ autograd
+_Function = None
+
+
+def _function():
+    """The autograd.Function, built on first use (torch is imported lazily)."""
+    global _Function
+    if _Function is not None:
+        return _Function
+    torch = _torch()
+
+    class FlashAttentionFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, scale, causal, window):
+            o, lse = attention_fwd(q, k, v, scale, causal, window=window)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.scale, ctx.causal, ctx.window = scale, causal, window
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv = attention_bwd(q, k, v, o, lse, do.contiguous(), ctx.scale, ctx.causal,
+                                       window=ctx.window)
+            return dq, dk, dv, None, None, None
+
+    _Function = FlashAttentionFunction
+    return _Function
+
+
+def attention(q, k, v, scale=None, causal=False, window=0):
+    """Differentiable exact attention: softmax(scale q k^T [causal, window]) v.
+
+    q [B, H, N, d], k and v [B, H_kv, N, d] (H_kv dividing H), fp16 or bf16,
+    contiguous device tensors; scale defaults to 1/sqrt(d).  The same result
+    as torch.nn.functional.scaled_dot_product_attention(q, k, v,
+    is_causal=causal, scale=scale, enable_gqa=True) up to rounding, computed
+    by libfa's kernels in both directions."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    return _function().apply(q.contiguous(), k.contiguous(), v.contiguous(),
+                             _default_scale(q.shape[-1], scale), bool(causal), int(window))

@@ -172,6 +172,8 @@ def test_binding_rejects_host_tensors():
     import torch
     q = torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
+        fa.attention(q, q, q)
+    with pytest.raises(ValueError):
         fa.attention_fwd(q, q, q)
     with pytest.raises(ValueError):
         fa.fa_fwd(q.float(), q, q, q, torch.zeros(1, 1, 16), 0.1, False)
