@@ -170,9 +170,20 @@ def attn_fwd_tiled(q, k, v, scale: float, causal: bool, br: int, bc: int):
     return o, lse
 
 
-def attn_decode(q, k, v, scale: float, nthreads: int = 0):
+def attn_decode(q, k, v, scale: float, nthreads: int = 0, kv_lens=None):
     """Single-token decode.  q [..., H, d] (or [..., H, 1, d]), k/v [..., H_kv, nkv, d]
-    (H_kv may divide H); returns o [..., H, d] and lse [..., H]."""
+    (H_kv may divide H); returns o [..., H, d] and lse [..., H].
+
+    kv_lens (q, k, v of shape [B, H, 1, d] / [B, H_kv, nkv, d]): sequence b attends
+    to its first kv_lens[b] keys only (a padded cache of ragged histories); a
+    sequence with no keys gets o = 0, lse = -inf."""
+    if kv_lens is not None:
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        lens = [int(x) for x in np.asarray(kv_lens).reshape(-1)]
+        assert k.ndim == 4 and len(lens) == k.shape[0]
+        outs = [attn_decode(q[b:b + 1], k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]], scale,
+                            nthreads) for b in range(k.shape[0])]
+        return (np.concatenate([o for o, _ in outs]), np.concatenate([l for _, l in outs]))
     q, k, v = _f64(q), _f64(k), _f64(v)
     nkv, d = k.shape[-2:]
     klead = k.shape[:-2]

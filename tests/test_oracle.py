@@ -452,6 +452,31 @@ def test_decode_matches_torch_and_forward():
     assert np.array_equal(of[:, :, 0], o) and np.array_equal(lsef[:, :, 0], lse)
 
 
+def test_decode_ragged_lengths():
+    """Per-sequence history lengths ("FlashAttention ontleed", § "Interactie met de
+    KV-cache tijdens inferentie": K and V span each sequence's own history)."""
+    b, h, hkv, nkv, d = 4, 4, 2, 50, 8
+    q, k, v = rand(b, h, 1, d), rand(b, hkv, nkv, d), rand(b, hkv, nkv, d)
+    full = oracle.attn_decode(q, k, v, 0.3)
+    same = oracle.attn_decode(q, k, v, 0.3, kv_lens=[nkv] * b)
+    assert all(np.array_equal(x, y) for x, y in zip(full, same))
+    lens = [50, 1, 0, 17]
+    o, lse = oracle.attn_decode(q, k, v, 0.3, kv_lens=lens)
+    # torch with a key-padding mask
+    mask = torch.from_numpy(np.arange(nkv)[None, :] < np.array(lens)[:, None])[:, None, None, :]
+    t = [torch.from_numpy(a) for a in (q, k, v)]
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, attn_mask=mask, scale=0.3,
+                                                           enable_gqa=True).numpy()[:, :, 0]
+    for bi in (0, 1, 3):
+        assert np.max(np.abs(o[bi] - ref[bi])) <= 1e-13
+    # one key: o is that key's value row, lse its scaled score
+    assert np.array_equal(o[1], np.repeat(v[1, :, 0], h // hkv, axis=0))
+    assert np.max(np.abs(lse[1] - 0.3 * np.einsum("hd,hd->h", q[1, :, 0],
+                                                  np.repeat(k[1, :, 0], h // hkv, axis=0)))) <= 1e-14
+    # no keys: o = 0, lse = -inf
+    assert not np.any(o[2]) and np.all(lse[2] == -np.inf)
+
+
 @pytest.mark.parametrize("nkv,splits", [(100, 1), (100, 3), (1024, 16), (1000, 16), (5, 16)])
 def test_merge_of_any_partition_equals_full_row(nkv, splits):
     d = 16
