@@ -24,7 +24,10 @@ workloads, outside the step (they do not enter value or ms_per_step):
     bf16, 16 chunks; GB/s of algorithmic bytes, K and V counted once per
     key/value head;
   * fa_fwd_ex, causal sliding window of 1024 keys: B=1 H=32 N=8192 d=128
-    bf16; TFLOP/s of useful work, 4 d FLOPs per visible (query, key) pair.
+    bf16; TFLOP/s of useful work, 4 d FLOPs per visible (query, key) pair;
+  * fa_decode_varlen, the grouped-head decode cache with ragged histories
+    (lengths uniform in [1, 16384], seeded); GB/s of the bytes the lengths
+    select (each sequence's K and V rows once per key/value head, q, o).
 --copy-calibration BYTES only copies a BYTES-sized device buffer 5 times
 (a plain copy kernel of known traffic, used to scale HBM byte counters).
 """
@@ -131,7 +134,17 @@ def measure_extensions(fa, torch, dev, reps: int):
     out.append({"workload": w.name, "entry": "fa_decode_ex", "bound": "hbm",
                 "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4)})
-    del q, k, v, o, lse, ws
+    from synth_inputs import ragged_lengths
+    lens_h = ragged_lengths(w.B, w.Nkv, w.seed)
+    lens = lens_h.to(dev)
+    ms = time_calls(torch, lambda: fa.fa_decode_varlen(q, k, v, lens, o, lse, w.scale, w.splits,
+                                                       ws), reps)
+    nbytes = (2 * w.Hkv * int(lens_h.sum()) * w.d + 2 * w.B * w.H * w.d) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out.append({"workload": w.name + "_ragged", "entry": "fa_decode_varlen", "bound": "hbm",
+                "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4)})
+    del q, k, v, o, lse, ws, lens
     torch.cuda.empty_cache()
     return out
 

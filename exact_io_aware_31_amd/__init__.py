@@ -9,6 +9,8 @@ Low-level functions carry the C names and take caller-allocated tensors:
     fa_fwd(q, k, v, o, lse, scale, causal)
     fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, causal)
     fa_decode(q, k, v, o, lse, scale, num_splits, workspace)
+    fa_decode_varlen(q, k, v, kv_lens, o, lse, scale, num_splits, workspace): decode
+        over a padded cache of ragged per-sequence histories
     fa_fwd_ex / fa_bwd_ex / fa_decode_ex: the same with grouped key/value heads
         (k, v with H_kv heads dividing H) and, forward and backward, a causal
         sliding window (window=w: key j visible to query i iff i - w < j <= i)
@@ -73,6 +75,8 @@ def load_library(path: str = LIB_PATH):
     lib.fa_bwd_ex.restype = i
     lib.fa_decode_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, i, vp]
     lib.fa_decode_ex.restype = i
+    lib.fa_decode_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, i, vp]
+    lib.fa_decode_varlen.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -228,6 +232,23 @@ def fa_decode_ex(q, k, v, o, lse, scale: float, num_splits: int, workspace, stre
     _check(load_library().fa_decode_ex(*args, B, H, hkv, Nkv, d, float(scale), int(num_splits),
                                        _dev(workspace, "workspace"), nbytes, _dt_code(k),
                                        _stream(k, stream)), "fa_decode_ex")
+
+
+def fa_decode_varlen(q, k, v, kv_lens, o, lse, scale: float, num_splits: int, workspace,
+                     stream=None):
+    """fa_decode_ex over a padded cache of ragged histories: sequence b attends to its first
+    kv_lens[b] keys (kv_lens: device int32 [B])."""
+    torch = _torch()
+    B, H, _, d = q.shape
+    hkv = _kv_heads(q, k)
+    Nkv = k.shape[2]
+    args = [_dev(q, "q", k.dtype, (B, H, 1, d)), _dev(k, "k"), _dev(v, "v", k.dtype, k.shape),
+            _dev(kv_lens, "kv_lens", torch.int32, (B,)), _dev(o, "o", k.dtype, (B, H, 1, d)),
+            _dev(lse, "lse", torch.float32, (B, H)) if lse is not None else ctypes.c_void_p(0)]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fa_decode_varlen(*args, B, H, hkv, Nkv, d, float(scale),
+                                           int(num_splits), _dev(workspace, "workspace"), nbytes,
+                                           _dt_code(k), _stream(k, stream)), "fa_decode_varlen")
 
 
 # ------------------------------------------------------------------ convenience

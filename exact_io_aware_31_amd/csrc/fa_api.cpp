@@ -43,6 +43,31 @@ fa_status check_ext(int H, int H_kv, int window, int causal) {
   return FA_OK;
 }
 
+// Shared body of fa_decode_ex and fa_decode_varlen (kv_lens may be null).
+fa_status decode_impl(const void* q, const void* k, const void* v, const int* kv_lens, void* o,
+                      float* lse, int B, int H, int H_kv, int Nkv, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes, fa_dtype dt,
+                      void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  fa_status st = check_common(B, H, Nkv, d, scale, dt);
+  if (st != FA_OK) return st;
+  if ((st = check_ext(H, H_kv, 0, 0)) != FA_OK) return st;
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  if ((long long)B * H * num_splits > kMaxGrid) return FA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits))
+    return FA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             fa::decode_part_o_bytes(B, H, d, num_splits));
+  fa::DecodeArgs a{q, k, v, o, lse, part_o, part_lse, B, H, Nkv, d, num_splits, H_kv, kv_lens,
+                   scale, to_dt(dt)};
+  return fa::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK
+                                                                                : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,27 +128,21 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
   return fa::decode_part_o_bytes(B, H, d, num_splits) + fa::decode_part_lse_bytes(B, H, num_splits);
 }
 
+fa_status fa_decode_varlen(const void* q, const void* k, const void* v, const int* kv_lens,
+                           void* o, float* lse, int B, int H, int H_kv, int Nkv, int d,
+                           float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                           fa_dtype dt, void* stream) {
+  if (!kv_lens) return FA_ERR_NULL;
+  if (!aligned(kv_lens, 4)) return FA_ERR_ALIGN;
+  return decode_impl(q, k, v, kv_lens, o, lse, B, H, H_kv, Nkv, d, scale, num_splits, workspace,
+                     workspace_bytes, dt, stream);
+}
+
 fa_status fa_decode_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                        int H, int H_kv, int Nkv, int d, float scale, int num_splits,
                        void* workspace, size_t workspace_bytes, fa_dtype dt, void* stream) {
-  if (!q || !k || !v || !o) return FA_ERR_NULL;
-  fa_status st = check_common(B, H, Nkv, d, scale, dt);
-  if (st != FA_OK) return st;
-  if ((st = check_ext(H, H_kv, 0, 0)) != FA_OK) return st;
-  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
-  if ((long long)B * H * num_splits > kMaxGrid) return FA_ERR_SHAPE;
-  if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits))
-    return FA_ERR_WORKSPACE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      (lse && !aligned(lse, 4)) || !aligned(workspace, 16))
-    return FA_ERR_ALIGN;
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             fa::decode_part_o_bytes(B, H, d, num_splits));
-  fa::DecodeArgs a{q, k, v, o, lse, part_o, part_lse, B, H, Nkv, d, num_splits, H_kv, scale,
-                   to_dt(dt)};
-  return fa::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK
-                                                                                : FA_ERR_HIP;
+  return decode_impl(q, k, v, nullptr, o, lse, B, H, H_kv, Nkv, d, scale, num_splits, workspace,
+                     workspace_bytes, dt, stream);
 }
 
 fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

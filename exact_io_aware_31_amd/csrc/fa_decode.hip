@@ -77,8 +77,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <typename T, int D, int G>
 __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    float* __restrict__ part_o, float* __restrict__ part_lse, int Nkv, int splits, int chunk,
-    int group, float c) {
+    const int* __restrict__ kv_lens, float* __restrict__ part_o, float* __restrict__ part_lse,
+    int Nkv, int splits, int Hkv, int group, float c) {
   using v8 = typename Vec<T>::v8;
   constexpr int LPK = D / 8;                 // lanes per key row
   constexpr int KPI = DEC_THREADS / LPK;     // key rows per workgroup step
@@ -93,8 +93,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
   const int h0 = kvbh * group + G * (wg % per_kv);   // first query head (over B x H)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = tid / LPK, col = tid % LPK;
+  // This sequence's history: its first kv_lens[b] keys (clamped to the cache),
+  // cut into `splits` chunks of ceil(len / splits) keys.
+  const int len = kv_lens ? min(max(kv_lens[kvbh / Hkv], 0), Nkv) : Nkv;
+  const int chunk = (len + splits - 1) / splits;
   const int k_lo = split * chunk;
-  const int k_hi = min(Nkv, k_lo + chunk);
+  const int k_hi = min(len, k_lo + chunk);
 
   if (k_lo >= k_hi) {  // empty chunk: weight zero in the merge
 #pragma unroll
@@ -255,6 +259,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   float big = -INFINITY;
   for (int s = lane; s < splits; s += 64) big = fmaxf(big, pl[s]);
   big = wave_max(big);
+  if (big == -INFINITY) {  // no key at all (an empty history): O = 0, lse = -inf
+    for (int i = lane; i < D; i += 64) O[(size_t)bh * D + i] = (T)0.f;
+    if (LSE && lane == 0) LSE[bh] = -INFINITY;
+    return;
+  }
   constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
@@ -274,12 +283,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
 
 template <typename T, int D, int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
-  const int chunk = (a.Nkv + a.splits - 1) / a.splits;
   const float c = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(a.B * a.H / G * a.splits),
                      dim3(DEC_THREADS), 0, s, static_cast<const T*>(a.q),
-                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.part_o, a.part_lse,
-                     a.Nkv, a.splits, chunk, a.H / a.Hkv, c);
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.kv_lens, a.part_o,
+                     a.part_lse, a.Nkv, a.splits, a.Hkv, a.H / a.Hkv, c);
   return hipGetLastError();
 }
 

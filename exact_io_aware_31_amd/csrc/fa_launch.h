@@ -40,6 +40,7 @@ struct DecodeArgs {
   float* part_lse;          // [B,H,S] float32 workspace
   int B, H, Nkv, d, splits;
   int Hkv;                  // key/value heads (k, v are [B,Hkv,Nkv,d])
+  const int* kv_lens;       // device int32 [B] history lengths, or null (all Nkv)
   float scale;
   DType dt;
 };

@@ -162,6 +162,24 @@ fa_status fa_decode_ex(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int H_kv, int Nkv, int d, float scale, int num_splits,
                        void* workspace, size_t workspace_bytes, fa_dtype dt, void* stream);
 
+/*
+ * Decode over a padded cache of ragged histories: every sequence of the batch
+ * has its own history length ("FlashAttention ontleed", § "Interactie met de
+ * KV-cache tijdens inferentie": K and V span each conversation's history).
+ * As fa_decode_ex, plus
+ *   kv_lens : device int32 [B], 4-byte aligned, read by the kernels:
+ *             sequence b attends to its first kv_lens[b] keys of the cache
+ *             (values are clamped to [0, Nkv]); its history is cut into
+ *             num_splits chunks of ceil(kv_lens[b] / num_splits) keys.  A
+ *             sequence with no keys gets o = 0 and lse = -inf.
+ *   k, v    : [B, H_kv, Nkv, d], Nkv the cache length (the longest history).
+ * kv_lens NULL is FA_ERR_NULL.
+ */
+fa_status fa_decode_varlen(const void* q, const void* k, const void* v, const int* kv_lens,
+                           void* o, float* lse, int B, int H, int H_kv, int Nkv, int d,
+                           float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                           fa_dtype dt, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status s);
 

@@ -95,6 +95,14 @@ def attention_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: i
     return q, k, v, do
 
 
+def ragged_lengths(B: int, Nkv: int, seed: int):
+    """Seeded history lengths for a padded cache of B sequences, uniform in [1, Nkv]
+    (int32, on the host)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    return torch.randint(1, Nkv + 1, (B,), generator=gen, dtype=torch.int32)
+
+
 def workload_inputs(w: Workload, device="cpu"):
     """Inputs of a named workload (decode: q is [B,H,1,d])."""
     hkv = w.Hkv or None

@@ -36,7 +36,8 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_decode", "fa_fwd_ex", "fa_bwd_ex",
-                          "fa_decode_ex", "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes",
+                          "fa_decode_ex", "fa_decode_varlen", "fa_bwd_workspace_bytes",
+                          "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/fa.h but not exported"
@@ -158,6 +159,19 @@ def test_window_validation(lib, call):
     assert call(lib, window=-1) == ERR["FA_ERR_SHAPE"]
     assert call(lib, window=4, causal=0) == ERR["FA_ERR_UNSUPPORTED"]
     assert call(lib, d=96, window=4) == ERR["FA_ERR_UNSUPPORTED"]
+
+
+def test_decode_varlen_validation(lib):
+    def call(kv_lens=P, **kw):
+        a = dict(B=2, H=8, H_kv=2, Nkv=100, d=128, splits=4)
+        a.update(kw)
+        return lib.fa_decode_varlen(P, P, P, kv_lens, P, P, a["B"], a["H"], a["H_kv"], a["Nkv"],
+                                    a["d"], 0.1, a["splits"], P, 1 << 30, 1, NULL)
+    assert call(kv_lens=NULL) == ERR["FA_ERR_NULL"]
+    assert call(kv_lens=P_ODD) == ERR["FA_ERR_ALIGN"]
+    assert call(H_kv=3) == ERR["FA_ERR_SHAPE"]
+    assert call(splits=0) == ERR["FA_ERR_SPLITS"]
+    assert call(d=32) == ERR["FA_ERR_UNSUPPORTED"]
 
 
 def test_bwd_ex_workspace_is_per_query_head(lib):

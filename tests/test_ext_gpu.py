@@ -129,3 +129,32 @@ def test_decode_ex(B, H, Hkv, Nkv, splits, d, dtype):
     o_ref, lse_ref = oracle.attn_decode(q, k, v, scale)
     check_max_abs(host64(o)[:, :, 0], o_ref, dtype, "O")
     check_max_abs(host64(lse), lse_ref, dtype, "lse")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hkv,splits", [(2, 4), (8, 16), (1, 1)])
+def test_decode_varlen(Hkv, splits, d, dtype):
+    B, H, Nkv = 6, 8, 700
+    lens = [700, 1, 0, 333, 64, 699]
+    seed = 9750 + Hkv + splits + d
+    announce(f"decode_varlen B{B} H{H} Hkv{Hkv} Nkv{Nkv} lens={lens} d{d} splits={splits} "
+             f"{dtype} seed={seed}")
+    q, k, v = attention_inputs(B, H, 1, d, dtype, seed, "cpu", Nkv=Nkv, Hkv=Hkv)
+    scale = d ** -0.5
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    kv_lens = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o = nan_like(qd)
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device=DEV)
+    ws = fa.decode_workspace(kd, splits, heads=H)
+    ws.fill_(0xFF)
+    fa.fa_decode_varlen(qd, kd, vd, kv_lens, o, lse, scale, splits, ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_decode(q, k, v, scale, kv_lens=lens)
+    got_o, got_lse = host64(o)[:, :, 0], host64(lse)
+    for b, n in enumerate(lens):
+        if n == 0:  # no keys: o = 0, lse = -inf
+            assert not np.any(got_o[b]) and np.all(got_lse[b] == -np.inf)
+            continue
+        check_max_abs(got_o[b], o_ref[b], dtype, f"O seq {b} (len {n})")
+        check_max_abs(got_lse[b], lse_ref[b], dtype, f"lse seq {b} (len {n})")
