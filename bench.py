@@ -13,7 +13,7 @@ HIP events recorded on the stream its kernels run on (torch's current
 stream, which the binding hands to the library).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--only fwd|bwd|decode|ext]
+                       [--only fwd|bwd|decode|ext] [--no-ext]
 --only runs a single entry point per step (for per-kernel profiling); the
 JSON line then carries only that entry's figures.  --only ext runs only the
 extension workloads.
@@ -28,6 +28,7 @@ workloads, outside the step (they do not enter value or ms_per_step):
   * fa_decode_varlen, the grouped-head decode cache with ragged histories
     (lengths uniform in [1, 16384], seeded); GB/s of the bytes the lengths
     select (each sequence's K and V rows once per key/value head, q, o).
+--no-ext skips them (profiles of the step's kernels alone).
 --copy-calibration BYTES only copies a BYTES-sized device buffer 5 times
 (a plain copy kernel of known traffic, used to scale HBM byte counters).
 """
@@ -176,6 +177,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--only", choices=("fwd", "bwd", "decode", "ext"), default=None)
+    ap.add_argument("--no-ext", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -304,7 +306,7 @@ def main():
         "rooflines": roofs,
         "wall_s_timed": round(t_wall, 3),
     }
-    if args.only is None:
+    if args.only is None and not args.no_ext:
         out["extensions"] = measure_extensions(fa, torch, dev, max(5, args.steps // 2))
     if args.only is not None:
         out["only"] = args.only
