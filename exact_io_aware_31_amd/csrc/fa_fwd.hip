@@ -10,8 +10,10 @@
 // lse = m + ln(l).
 //
 // MI355X mapping (not the pages' A100 tile rule):
-//   * NW waves x (32 * QG) query rows per workgroup, two waves per SIMD;
-//     64-key tiles.
+//   * NW waves x 32 query rows per workgroup, two waves per SIMD; 64-key
+//     tiles.  Eight-wave workgroups (one per CU) are the default; when the
+//     grid of 256-row blocks is too small to give every CU several of them,
+//     four-wave workgroups run two per CU instead.
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
 //     each lane then owns ONE query row per 32-row group (column l % 32) and
 //     16 of its scores per 32-key block, so the row max / row sum are in-lane
@@ -23,7 +25,9 @@
 //     read (ds_read_b64_tr_b16), so V is never transposed in memory.
 //   * K and V tiles reach LDS by direct global-to-LDS loads
 //     (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS
-//     base + 16 * lane), two tiles ahead of their use, in a three-deep ring.
+//     base + 16 * lane) into a ring of tiles: three deep, two tiles ahead of
+//     their use, for eight waves; two deep, one tile ahead, for four (so
+//     that two workgroups fit in LDS).
 //     No registers hold staged data and no LDS store instructions are issued;
 //     each wave waits for its own loads before the tile's barrier.  Tiles are
 //     stored unpadded with 16-byte chunk c of row r at chunk c ^ sw(r), which
@@ -50,18 +54,9 @@
 #include "fa_launch.h"
 #include "fa_tile.h"
 
-#ifndef FA_FWD_NW
-#define FA_FWD_NW 8
-#endif
-#ifndef FA_FWD_QG
-#define FA_FWD_QG 1
-#endif
-
 namespace fa {
 
-constexpr int FWD_NW = FA_FWD_NW;  // waves per workgroup
-constexpr int FWD_QG = FA_FWD_QG;  // 32-row query groups per wave
-constexpr int FWD_BR = FWD_NW * 32 * FWD_QG;
+constexpr int FWD_QG = 1;  // 32-row query groups per wave
 constexpr int FWD_BC = 64;
 constexpr float FWD_RESCALE_SLACK = 8.0f;  // log2 units
 
@@ -76,14 +71,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   // The sliding-window code exists only in the WIN instantiation (window is
   // then >= 1 and the mask causal); elsewhere it folds away.
   if constexpr (!WIN) window = 0;
-  constexpr int NT = NW * 64;
   constexpr int BR = NW * 32 * QG, BC = FWD_BC;
   constexpr int SPW = BC * D * 2 / 1024 / NW;  // tile load segments per wave (vmcnt units)
-  static_assert(NT == 512, "two waves per SIMD at one workgroup per CU");
-  // Three-deep ring of K and V tiles (separate arrays, so every access names
-  // its buffer statically and the compiler sees which loads it depends on).
-  __shared__ __attribute__((aligned(1024))) T K0[BC * D], K1[BC * D], K2[BC * D];
-  __shared__ __attribute__((aligned(1024))) T V0[BC * D], V1[BC * D], V2[BC * D];
+  constexpr int RING = NW == 8 ? 3 : 2;         // tiles in the LDS ring
+  static_assert(NW == 8 || NW == 4, "one eight-wave or two four-wave workgroups per CU");
+  // The ring of K and V tiles (separate arrays, so every access names its
+  // buffer statically and the compiler sees which loads it depends on).
+  __shared__ __attribute__((aligned(1024))) T K0[BC * D], K1[BC * D], K2[RING > 2 ? BC * D : 1];
+  __shared__ __attribute__((aligned(1024))) T V0[BC * D], V1[BC * D], V2[RING > 2 ? BC * D : 1];
 
   // Work item: XCD-local heads, heaviest causal query blocks first.
   const int p = blockIdx.x;
@@ -155,10 +150,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     for (int nb = 0; nb < D / 32; ++nb)
       voff[t][nb] = tile_off<D>(8 * t + 4 * hh + (li >> 2), 32 * nb + 16 * (grp & 1) + 4 * (li & 3));
 
-  // Tiles 0 and 1 in flight; wait for tile 0 (vmcnt counts this wave's loads).
+  // Tiles 0 .. RING-2 in flight; wait for tile 0 (vmcnt counts this wave's loads).
   load_kv(Kh, K0, kbase);
   load_kv(Vh, V0, kbase);
-  if (nt > 1) {
+  if (RING > 2 && nt > 1) {
     load_kv(Kh, K1, kbase + BC);
     load_kv(Vh, V1, kbase + BC);
     wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
@@ -169,14 +164,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   // fenced barrier would also wait for the loads of the tile after next).
   bare_barrier();
 
-  // One tile: tile j+2 starts loading into the buffer tile j-1 used, tile j is
-  // computed, and before the barrier this wave's loads of tile j+1 are done.
+  // One tile: tile j + RING - 1 starts loading into the buffer tile j-1
+  // used, tile j is computed, and before the barrier this wave's loads of
+  // tile j+1 are done.
   auto tile_step = [&](int j, const T* __restrict__ kt, const T* __restrict__ vt, T* kn, T* vn) {
     const int kb = kbase + j * BC;
-    const bool more = j + 2 < nt;
+    const bool more = j + RING - 1 < nt;
     if (more) {
-      load_kv(Kh, kn, kb + 2 * BC);
-      load_kv(Vh, vn, kb + 2 * BC);
+      load_kv(Kh, kn, kb + (RING - 1) * BC);
+      load_kv(Vh, vn, kb + (RING - 1) * BC);
     }
     bool active[QG];
     bool any_active = false;
@@ -309,16 +305,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
 
     // Tile j+1 has landed (this wave's share) and every LDS read of tile j
     // has returned; after the barrier no wave reads tile j's buffer again, so
-    // the next step may start loading tile j+3 into it.
-    if (more) wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
+    // the next step may start loading into it.
+    if (RING > 2 && more) wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
     else wait_counts<FA_VMCNT_LGKM0(0)>();
     bare_barrier();
   };
-  // Unrolled by three so each step names its ring buffers statically.
-  for (int j = 0; j < nt; j += 3) {
-    tile_step(j, K0, V0, K2, V2);
-    if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
-    if (j + 2 < nt) tile_step(j + 2, K2, V2, K1, V1);
+  // Unrolled by the ring depth so each step names its ring buffers statically.
+  if constexpr (RING == 3) {
+    for (int j = 0; j < nt; j += 3) {
+      tile_step(j, K0, V0, K2, V2);
+      if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
+      if (j + 2 < nt) tile_step(j + 2, K2, V2, K1, V1);
+    }
+  } else {
+    for (int j = 0; j < nt; j += 2) {
+      tile_step(j, K0, V0, K1, V1);
+      if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
+    }
   }
 
   // Epilogue: O = O / l, lse = (m + log2 l) ln 2.
@@ -342,16 +345,30 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool WIN>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-  const int nqb = (a.N + FWD_BR - 1) / FWD_BR;
+template <typename T, int D, bool CAUSAL, bool WIN, int NW>
+static hipError_t launch_fwd_nw(const FwdArgs& a, hipStream_t s) {
+  const int br = NW * 32 * FWD_QG;
+  const int nqb = (a.N + br - 1) / br;
   const int total = a.B * a.H * nqb;
   const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, WIN, FWD_NW, FWD_QG>), dim3(total), dim3(FWD_NW * 64),
-                     0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, WIN, NW, FWD_QG>), dim3(total), dim3(NW * 64), 0, s,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.N, nqb, total,
                      a.H / a.Hkv, WIN ? a.window : 0, c);
   return hipGetLastError();
+}
+
+// Fewer than four 256-row blocks per CU (1024 on the 256 CUs): four-wave
+// workgroups, two per CU, keep the SIMDs fed (measured: B4 H16 N2048
+// causal runs 13% faster so; at B1 H32 N8192, 1024 blocks, the eight-wave
+// shape is 4.5% faster, as its K/V tiles serve twice the rows).
+constexpr long FWD_SMALL_GRID = 1024;
+
+template <typename T, int D, bool CAUSAL, bool WIN>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
+  const long blocks256 = (long)a.B * a.H * ((a.N + 255) / 256);
+  return blocks256 < FWD_SMALL_GRID ? launch_fwd_nw<T, D, CAUSAL, WIN, 4>(a, s)
+                                    : launch_fwd_nw<T, D, CAUSAL, WIN, 8>(a, s);
 }
 
 template <typename T, int D>
