@@ -12,9 +12,13 @@
 //
 // The path is HBM-bound (about 1 flop per byte), so the kernels are written
 // for bandwidth: 16-byte coalesced loads (a run of d/8 lanes reads one
-// 2*d-byte key row), several loads in flight per lane, fp32 FMAs on the
-// VALU (the matrix cores would idle with one query column), and the chunk's
-// scores kept in LDS between the K pass and the V pass.
+// 2*d-byte key row), several loads in flight per lane, packed dot products
+// on the VALU (the matrix cores would idle with one query column), and the
+// chunk's scores kept in LDS between the K pass and the V pass.  Scores are
+// v_dot2_f32 over pairs of stored elements (exact products, fp32 sums);
+// the probabilities are rounded to the storage type, as the fused forward
+// pass rounds P for its P V product, and the output accumulates
+// v_dot2_f32 over pairs of keys: (v_a[i], v_b[i]) . (p_a, p_b).
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -24,10 +28,24 @@ constexpr int DEC_THREADS = 256;
 constexpr int DEC_SUB = 1024;  // keys whose scores are held in LDS at a time
 constexpr int DEC_UNROLL = 8;  // key rows in flight per lane
 
-template <typename T>
-__device__ __forceinline__ void widen8(const typename Vec<T>::v8& x, float* f) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = (float)x[i];
+// acc + a.x b.x + a.y b.y in fp32 (v_dot2_f32_bf16 / v_dot2_f32_f16).
+__device__ __forceinline__ float dot2(__bf16 __attribute__((ext_vector_type(2))) a,
+                                      __bf16 __attribute__((ext_vector_type(2))) b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+}
+__device__ __forceinline__ float dot2(_Float16 __attribute__((ext_vector_type(2))) a,
+                                      _Float16 __attribute__((ext_vector_type(2))) b, float acc) {
+  return __builtin_amdgcn_fdot2(a, b, acc, false);
+}
+// sum_i a[i] b[i] over 8 elements: four packed dot products.  The pairs are
+// taken with element shuffles: fed bit casts of the packed 32-bit words
+// instead, this compiler keeps only the first of several such dot products.
+template <typename V8>
+__device__ __forceinline__ float dot8(V8 a, V8 b) {
+  float acc = dot2(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), 0.f);
+  acc = dot2(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), acc);
+  acc = dot2(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), acc);
+  return dot2(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), acc);
 }
 
 // x + (x of the lane chosen by the DPP pattern), all in registers.
@@ -113,13 +131,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
   const size_t hoff = (size_t)kvbh * Nkv * D;
   const T* __restrict__ Kh = K + hoff;
   const T* __restrict__ Vh = V + hoff;
-  float qv[G][8];
+  // The query elements stay packed; scores are scaled by c after the sum,
+  // so they come out in log2 units.
+  v8 qv[G];
 #pragma unroll
-  for (int gh = 0; gh < G; ++gh) {
-    widen8<T>(ld16<v8>(Q + (size_t)(h0 + gh) * D + 8 * col), qv[gh]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qv[gh][i] *= c;  // scores come out in log2 units
-  }
+  for (int gh = 0; gh < G; ++gh) qv[gh] = ld16<v8>(Q + (size_t)(h0 + gh) * D + 8 * col);
 
   float o[G][8], m_run[G], l_run[G];
 #pragma unroll
@@ -144,15 +160,10 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
       }
 #pragma unroll
       for (int u = 0; u < DEC_UNROLL; ++u) {
-        float kf[8];
-        widen8<T>(kr[u], kf);
         const int key = kk + u * KPI;
 #pragma unroll
         for (int gh = 0; gh < G; ++gh) {
-          float dot = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(qv[gh][i], kf[i], dot);
-          dot = row_sum<LPK>(dot);
+          const float dot = row_sum<LPK>(dot8(kr[u], qv[gh])) * c;
           if (col == 0 && key < s1) sc[gh][key - s0] = dot;
         }
       }
@@ -178,12 +189,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
       alpha[gh] = fast_exp2(m_run[gh] - m_new[gh]);
     }
     __syncthreads();  // everyone has read red[]
-    // Probabilities (unnormalised) in place, and their sums.
+    // Probabilities (unnormalised, rounded to the storage type: the weights
+    // the V pass uses) in place, and their sums.
 #pragma unroll
     for (int gh = 0; gh < G; ++gh) {
       float ps = 0.f;
       for (int i = tid; i < s1 - s0; i += DEC_THREADS) {
-        const float pe = fast_exp2(sc[gh][i] - m_new[gh]);
+        const float pe = (float)(T)fast_exp2(sc[gh][i] - m_new[gh]);
         sc[gh][i] = pe;
         ps += pe;
       }
@@ -210,16 +222,28 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
         const int key = min(kk + u * KPI, s1 - 1);
         vr[u] = ld16_stream<v8>(Vh + (size_t)key * D + 8 * col);
       }
+      // Keys in pairs (u, u+1): element i of the two value rows against the
+      // two probabilities, one packed dot product per element and head.
+      typedef T t2 __attribute__((ext_vector_type(2)));
+      static_assert(DEC_UNROLL % 2 == 0, "value rows are taken in pairs");
 #pragma unroll
-      for (int u = 0; u < DEC_UNROLL; ++u) {
-        const int key = kk + u * KPI;
-        float vf[8];
-        widen8<T>(vr[u], vf);
+      for (int u = 0; u < DEC_UNROLL; u += 2) {
+        const int ka = kk + u * KPI, kb = ka + KPI;
+        const v8 va = vr[u], vb = vr[u + 1];
+        t2 vp[8];
+        vp[0] = __builtin_shufflevector(va, vb, 0, 8);
+        vp[1] = __builtin_shufflevector(va, vb, 1, 9);
+        vp[2] = __builtin_shufflevector(va, vb, 2, 10);
+        vp[3] = __builtin_shufflevector(va, vb, 3, 11);
+        vp[4] = __builtin_shufflevector(va, vb, 4, 12);
+        vp[5] = __builtin_shufflevector(va, vb, 5, 13);
+        vp[6] = __builtin_shufflevector(va, vb, 6, 14);
+        vp[7] = __builtin_shufflevector(va, vb, 7, 15);
 #pragma unroll
         for (int gh = 0; gh < G; ++gh) {
-          const float pe = (key < s1) ? sc[gh][key - s0] : 0.f;
+          const t2 pp = {(T)((ka < s1) ? sc[gh][ka - s0] : 0.f), (T)((kb < s1) ? sc[gh][kb - s0] : 0.f)};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[gh][i] = __builtin_fmaf(pe, vf[i], o[gh][i]);
+          for (int i = 0; i < 8; ++i) o[gh][i] = dot2(vp[i], pp, o[gh][i]);
         }
       }
     }
