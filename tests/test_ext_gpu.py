@@ -158,3 +158,21 @@ def test_decode_varlen(Hkv, splits, d, dtype):
             continue
         check_max_abs(got_o[b], o_ref[b], dtype, f"O seq {b} (len {n})")
         check_max_abs(got_lse[b], lse_ref[b], dtype, f"lse seq {b} (len {n})")
+
+
+@pytest.mark.parametrize("H", [60, 64], ids=["4wave", "8wave"])
+def test_fwd_ex_both_workgroup_shapes(H):
+    """Grouped heads and a window at a grid of 1024 (eight-wave) or 960 (four-wave) blocks."""
+    B, N, d, dtype, window = 4, 1024, 128, torch.bfloat16, 300
+    Hkv = H // 4
+    seed = 9950 + H
+    announce(f"fwd_ex shapes B{B} H{H} Hkv{Hkv} N{N} d{d} window={window} seed={seed}")
+    q, k, v = attention_inputs(B, H, N, d, dtype, seed, "cpu", Hkv=Hkv)
+    scale = d ** -0.5
+    o, lse = run_fwd_ex(q.to(DEV), k.to(DEV), v.to(DEV), scale, True, window)
+    o_h, lse_h = host64(o), host64(lse)
+    for b, h in [(0, 0), (2, H // 2 + 1), (3, H - 1)]:
+        hk = h // (H // Hkv)
+        o_ref, lse_ref = oracle.attn_fwd(q[b, h], k[b, hk], v[b, hk], scale, True, window=window)
+        check_max_abs(o_h[b, h], o_ref, dtype, f"O head ({b},{h})")
+        check_max_abs(lse_h[b, h], lse_ref, dtype, f"lse head ({b},{h})")

@@ -90,3 +90,24 @@ def test_fwd_deterministic():
     o1, l1 = run_fwd(q, k, v, w.scale, True)
     o2, l2 = run_fwd(q, k, v, w.scale, True)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("H", [63, 64], ids=["4wave", "8wave"])
+def test_fwd_both_workgroup_shapes(H, causal, d, dtype):
+    """B4 N1024: 64 heads give 1024 blocks of 256 rows (eight-wave workgroups), 63 heads 1008
+    (four-wave workgroups, two per CU).  Whole heads spread over the grid against the oracle."""
+    B, N = 4, 1024
+    seed = 7300 + H + d + (1 if causal else 0)
+    announce(f"fwd shapes B{B} H{H} N{N} d{d} causal={causal} {dtype} seed={seed}")
+    q, k, v = attention_inputs(B, H, N, d, dtype, seed, "cpu")
+    scale = d ** -0.5
+    o, lse = run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal)
+    o_h, lse_h = host64(o), host64(lse)
+    assert np.all(np.isfinite(o_h)) and np.all(np.isfinite(lse_h)), "unwritten outputs"
+    for b, h in [(0, 0), (1, H // 2), (3, H - 1)]:
+        o_ref, lse_ref = oracle.attn_fwd(q[b, h], k[b, h], v[b, h], scale, causal)
+        check_max_abs(o_h[b, h], o_ref, dtype, f"O head ({b},{h})")
+        check_max_abs(lse_h[b, h], lse_ref, dtype, f"lse head ({b},{h})")
