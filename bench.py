@@ -28,7 +28,11 @@ workloads, outside the step (they do not enter value or ms_per_step):
   * fa_decode_varlen, the grouped-head decode cache with ragged histories
     (lengths uniform in [1, 16384], seeded); GB/s of the bytes the lengths
     select (each sequence's K and V rows once per key/value head, q, o).
---no-ext skips them (profiles of the step's kernels alone).
+The other forward/backward configurations (tiny fp16 forward B1 H1 N256 d64;
+B4 H16 N2048 d128 bf16 causal forward; B2 H16 N4096 d128 bf16 causal
+backward) are timed the same way under "configs" (TFLOP/s of 4 B H N^2 d
+forward and 10 B H N^2 d backward FLOPs, halved for causal, as the step).
+--no-ext skips both (profiles of the step's kernels alone).
 --copy-calibration BYTES only copies a BYTES-sized device buffer 5 times
 (a plain copy kernel of known traffic, used to scale HBM byte counters).
 """
@@ -146,6 +150,37 @@ def measure_extensions(fa, torch, dev, reps: int):
                 "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4)})
     del q, k, v, o, lse, ws, lens
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_configs(fa, torch, dev, reps: int):
+    """The forward and backward shapes the step does not time itself: the tiny fp16 forward,
+    the B4 H16 N2048 causal forward and the B2 H16 N4096 causal backward (useful-FLOP rates)."""
+    from synth_inputs import BWD_4K, FWD_2K, TINY_FWD, workload_inputs
+    out = []
+    for w in (TINY_FWD, FWD_2K, BWD_4K):
+        ins = workload_inputs(w, dev)
+        q, k, v = ins[:3]
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+        pairs = w.N * w.N / 2 if w.causal else w.N * w.N  # halved for causal, as the step
+        if w.kind == "fwd":
+            ms = time_calls(torch, lambda: fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal), reps)
+            flops = 4 * w.B * w.H * w.d * pairs
+        else:
+            do = ins[3]
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = fa.bwd_workspace(q)
+            ms = time_calls(torch, lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, w.scale,
+                                                     w.causal), reps)
+            flops = 10 * w.B * w.H * w.d * pairs
+        tf = flops / (ms * 1e-3) / 1e12
+        out.append({"workload": w.name, "entry": "fa_" + w.kind, "bound": "mfma",
+                    "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / PEAK_BF16_TFLOPS, 4), "ms": round(ms, 4)})
+        del ins, q, k, v, o, lse
     torch.cuda.empty_cache()
     return out
 
@@ -307,6 +342,7 @@ def main():
         "wall_s_timed": round(t_wall, 3),
     }
     if args.only is None and not args.no_ext:
+        out["configs"] = measure_configs(fa, torch, dev, max(5, args.steps // 2))
         out["extensions"] = measure_extensions(fa, torch, dev, max(5, args.steps // 2))
     if args.only is not None:
         out["only"] = args.only

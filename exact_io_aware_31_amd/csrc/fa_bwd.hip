@@ -300,22 +300,25 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
 }
 
 // ---------------------------------------------------------------- kernel 3
-constexpr int DQ_WAVES = 8;
-constexpr int DQ_BR = 32 * DQ_WAVES;  // query rows per workgroup
-constexpr int DQ_BC = 64;             // keys per tile
+// NW waves x 32 query rows per workgroup: eight waves (one workgroup per CU,
+// a three-deep ring) by default, four (two workgroups per CU, a two-deep
+// ring) when the grid of 256-row blocks is small, as in the forward pass.
+constexpr int DQ_BC = 64;  // keys per tile
 
-template <typename T, int D, bool CAUSAL, bool WIN>
-__global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
+template <typename T, int D, bool CAUSAL, bool WIN, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ drow,
     T* __restrict__ dQ, int N, int nqb, int total, int group, int window, float scale, float c) {
   using v8 = typename Vec<T>::v8;
   using v4 = typename Vec<T>::v4;
   if constexpr (!WIN) window = 0;  // window code only in the WIN instantiation
-  constexpr int NW = DQ_WAVES, BR = DQ_BR, BC = DQ_BC, NB = D / 32;
+  constexpr int BR = 32 * NW, BC = DQ_BC, NB = D / 32;
   constexpr int SPW = BC * D * 2 / 1024 / NW;  // tile load segments per wave (vmcnt units)
-  __shared__ __attribute__((aligned(1024))) T K0[BC * D], K1[BC * D], K2[BC * D];
-  __shared__ __attribute__((aligned(1024))) T V0[BC * D], V1[BC * D], V2[BC * D];
+  constexpr int RING = NW == 8 ? 3 : 2;         // tiles in the LDS ring
+  static_assert(NW == 8 || NW == 4, "one eight-wave or two four-wave workgroups per CU");
+  __shared__ __attribute__((aligned(1024))) T K0[BC * D], K1[BC * D], K2[RING > 2 ? BC * D : 1];
+  __shared__ __attribute__((aligned(1024))) T V0[BC * D], V1[BC * D], V2[RING > 2 ? BC * D : 1];
 
   // Work item: XCD-local heads, heaviest causal query blocks first.
   const int p = blockIdx.x;
@@ -367,10 +370,10 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
   const uint32_t rb = tile_row_base<D>(l32, hh);
   const uint32_t tb = tile_tr_base<D>(4 * hh + (li >> 2), 16 * (grp & 1) + 4 * (li & 3));
 
-  // Tiles 0 and 1 in flight; wait for tile 0.
+  // Tiles 0 .. RING-2 in flight; wait for tile 0.
   load_kv(Kh, K0, kbase);
   load_kv(Vh, V0, kbase);
-  if (nt > 1) {
+  if (RING > 2 && nt > 1) {
     load_kv(Kh, K1, kbase + BC);
     load_kv(Vh, V1, kbase + BC);
     wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
@@ -379,14 +382,15 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
   }
   bare_barrier();
 
-  // One tile: tile j+2 starts loading into the buffer tile j-1 used, tile j is
-  // computed, and before the barrier this wave's loads of tile j+1 are done.
+  // One tile: tile j + RING - 1 starts loading into the buffer tile j-1 used,
+  // tile j is computed, and before the barrier this wave's loads of tile j+1
+  // are done.
   auto tile_step = [&](int j, const T* __restrict__ kt, const T* __restrict__ vt, T* kn, T* vn) {
     const int kb = kbase + j * BC;
-    const bool more = j + 2 < nt;
+    const bool more = j + RING - 1 < nt;
     if (more) {
-      load_kv(Kh, kn, kb + 2 * BC);
-      load_kv(Vh, vn, kb + 2 * BC);
+      load_kv(Kh, kn, kb + (RING - 1) * BC);
+      load_kv(Vh, vn, kb + (RING - 1) * BC);
     }
     if (!CAUSAL || (kb <= qw0 + 31 && (window == 0 || kb + BC - 1 > qw0 - window))) {
       // Keys past the end and, on diagonal tiles, keys after the query are
@@ -459,15 +463,22 @@ __global__ __launch_bounds__(DQ_WAVES * 64, 1) void bwd_dq_kernel(
     }
     // Tile j+1 has landed (this wave's share) and every LDS read of tile j
     // has returned; after the barrier no wave reads tile j's buffer again.
-    if (more) wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
+    if (RING > 2 && more) wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
     else wait_counts<FA_VMCNT_LGKM0(0)>();
     bare_barrier();
   };
-  // Unrolled by three so each step names its ring buffers statically.
-  for (int j = 0; j < nt; j += 3) {
-    tile_step(j, K0, V0, K2, V2);
-    if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
-    if (j + 2 < nt) tile_step(j + 2, K2, V2, K1, V1);
+  // Unrolled by the ring depth so each step names its ring buffers statically.
+  if constexpr (RING == 3) {
+    for (int j = 0; j < nt; j += 3) {
+      tile_step(j, K0, V0, K2, V2);
+      if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
+      if (j + 2 < nt) tile_step(j + 2, K2, V2, K1, V1);
+    }
+  } else {
+    for (int j = 0; j < nt; j += 2) {
+      tile_step(j, K0, V0, K1, V1);
+      if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
+    }
   }
 
   // dQ = scale * dQ^T transposed back: lane writes row myq.
@@ -510,11 +521,19 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int nqb = (a.N + DQ_BR - 1) / DQ_BR;
+  // Fewer than four 256-row blocks per CU: four-wave workgroups, two per CU.
+  const bool small = (long)a.B * a.H * ((a.N + 255) / 256) < 1024;
+  const int br = small ? 128 : 256;
+  const int nqb = (a.N + br - 1) / br;
   const int dq_total = a.B * a.H * nqb;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, WIN>), dim3(dq_total), dim3(DQ_WAVES * 64), 0, s, q, k,
-                     v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group, window,
-                     a.scale, c);
+  if (small)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, WIN, 4>), dim3(dq_total), dim3(4 * 64), 0, s, q,
+                       k, v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
+                       window, a.scale, c);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, WIN, 8>), dim3(dq_total), dim3(8 * 64), 0, s, q,
+                       k, v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
+                       window, a.scale, c);
   return hipGetLastError();
 }
 
