@@ -247,9 +247,9 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
 
     // dV_w += P^T dO_i; the B operand comes from transpose reads of the dO tile.
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int kc = 0; kc < BQ / 16; ++kc)
 #pragma unroll
-      for (int kc = 0; kc < BQ / 16; ++kc) {
+      for (int nb = 0; nb < NB; ++nb) {
         const u32x2 d0 = lds_tr_at(dOs[0], (tbs ^ tile_tr_xor<D>(0, nb)) + 32 * D * kc);
         const u32x2 d1 = lds_tr_at(dOs[0], (tbs ^ tile_tr_xor<D>(1, nb)) + 32 * D * kc);
         const u32x4 cd = {d0[0], d0[1], d1[0], d1[1]};
@@ -271,9 +271,9 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     }
     // dK_w += dS^T Q_i (scale applied at the end), Q^T by transpose reads.
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int kc = 0; kc < BQ / 16; ++kc)
 #pragma unroll
-      for (int kc = 0; kc < BQ / 16; ++kc) {
+      for (int nb = 0; nb < NB; ++nb) {
         const u32x2 q0 = lds_tr_at(Qs[0], (tbs ^ tile_tr_xor<D>(0, nb)) + 32 * D * kc);
         const u32x2 q1 = lds_tr_at(Qs[0], (tbs ^ tile_tr_xor<D>(1, nb)) + 32 * D * kc);
         const u32x4 cq = {q0[0], q0[1], q1[0], q1[1]};
@@ -449,9 +449,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
             dsb[hf] = to_v8<T>(dsv);
           }
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
+          for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
+            for (int nb = 0; nb < NB; ++nb) {
               const int kc = 2 * sb + hf;
               const u32x2 lo = lds_tr_at(kt, (tbs ^ tile_tr_xor<D>(0, nb)) + 32 * D * kc);
               const u32x2 hi = lds_tr_at(kt, (tbs ^ tile_tr_xor<D>(1, nb)) + 32 * D * kc);

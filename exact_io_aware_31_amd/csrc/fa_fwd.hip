@@ -290,9 +290,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
 
       // O^T += V^T P^T; the V^T operand comes from two transpose reads.
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb)
+      for (int kc = 0; kc < BC / 16; ++kc)
 #pragma unroll
-        for (int kc = 0; kc < BC / 16; ++kc) {
+        for (int nb = 0; nb < D / 32; ++nb) {
           const u32x2 lo = lds_read_tr16(vt + 16 * kc * D + voff[0][nb]);
           const u32x2 hi = lds_read_tr16(vt + 16 * kc * D + voff[1][nb]);
           const u32x4 cat = {lo[0], lo[1], hi[0], hi[1]};
