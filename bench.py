@@ -210,7 +210,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--only", choices=("fwd", "bwd", "decode", "ext"), default=None)
     ap.add_argument("--no-ext", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
