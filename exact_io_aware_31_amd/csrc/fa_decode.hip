@@ -60,10 +60,10 @@ __device__ __forceinline__ float dpp_add(float x) {
 // within the 16-lane row.
 template <int WIDTH>
 __device__ __forceinline__ float row_sum(float x) {
-  static_assert(WIDTH == 8 || WIDTH == 16, "8- or 16-lane rows");
+  static_assert(WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "4-, 8- or 16-lane rows");
   x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
   x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
-  x = dpp_add<0x141>(x);  // row_half_mirror
+  if (WIDTH >= 8) x = dpp_add<0x141>(x);  // row_half_mirror
   if (WIDTH == 16) x = dpp_add<0x140>(x);  // row_mirror
   return x;
 }
@@ -98,8 +98,16 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
     const int* __restrict__ kv_lens, float* __restrict__ part_o, float* __restrict__ part_lse,
     int Nkv, int splits, int Hkv, int group, float c) {
   using v8 = typename Vec<T>::v8;
-  constexpr int LPK = D / 8;                 // lanes per key row
-  constexpr int KPI = DEC_THREADS / LPK;     // key rows per workgroup step
+  constexpr int LPK = D / 8;                 // lanes per value row (V pass)
+  constexpr int KPI = DEC_THREADS / LPK;     // value rows per workgroup step
+  // K pass: with one query head each lane dots 16 elements (two 16-byte
+  // loads) of a key row, so a row is summed over D / 16 lanes, one DPP step
+  // fewer per score (+1.3% at B64 H32 Nkv16384); with several heads the
+  // extra query registers would cost occupancy, so 8 elements per lane.
+  constexpr int KP = (G == 1) ? 2 : 1;       // 16-byte parts of a key row per lane
+  constexpr int LPKK = D / (8 * KP);         // lanes per key row (K pass)
+  constexpr int KPIK = DEC_THREADS / LPKK;   // key rows per workgroup step (K pass)
+  constexpr int UNK = DEC_UNROLL / KP;       // key rows in flight per lane
   constexpr int NWV = DEC_THREADS / 64;      // waves
   __shared__ float sc[G][DEC_SUB];
   __shared__ float red[G][NWV];
@@ -111,6 +119,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
   const int h0 = kvbh * group + G * (wg % per_kv);   // first query head (over B x H)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = tid / LPK, col = tid % LPK;
+  const int kslot = tid / LPKK, kcol = tid % LPKK;
   // This sequence's history: its first kv_lens[b] keys (clamped to the cache),
   // cut into `splits` chunks of ceil(len / splits) keys.
   const int len = kv_lens ? min(max(kv_lens[kvbh / Hkv], 0), Nkv) : Nkv;
@@ -133,9 +142,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
   const T* __restrict__ Vh = V + hoff;
   // The query elements stay packed; scores are scaled by c after the sum,
   // so they come out in log2 units.
-  v8 qv[G];
+  v8 qv[G][KP];
 #pragma unroll
-  for (int gh = 0; gh < G; ++gh) qv[gh] = ld16<v8>(Q + (size_t)(h0 + gh) * D + 8 * col);
+  for (int gh = 0; gh < G; ++gh)
+#pragma unroll
+    for (int pp = 0; pp < KP; ++pp) qv[gh][pp] = ld16<v8>(Q + (size_t)(h0 + gh) * D + 8 * (KP * kcol + pp));
 
   float o[G][8], m_run[G], l_run[G];
 #pragma unroll
@@ -149,22 +160,27 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(
   for (int s0 = k_lo; s0 < k_hi; s0 += DEC_SUB) {
     const int s1 = min(k_hi, s0 + DEC_SUB);
     // K pass: scores of keys s0..s1-1 for the G heads into LDS.
-    for (int kk = s0 + slot; kk < s1; kk += KPI * DEC_UNROLL) {
+    for (int kk = s0 + kslot; kk < s1; kk += KPIK * UNK) {
       // Rows past the sub-chunk are clamped to its last row (always valid);
       // their scores are never stored.
-      v8 kr[DEC_UNROLL];
+      v8 kr[UNK][KP];
 #pragma unroll
-      for (int u = 0; u < DEC_UNROLL; ++u) {
-        const int key = min(kk + u * KPI, s1 - 1);
-        kr[u] = ld16_stream<v8>(Kh + (size_t)key * D + 8 * col);
+      for (int u = 0; u < UNK; ++u) {
+        const int key = min(kk + u * KPIK, s1 - 1);
+#pragma unroll
+        for (int pp = 0; pp < KP; ++pp)
+          kr[u][pp] = ld16_stream<v8>(Kh + (size_t)key * D + 8 * (KP * kcol + pp));
       }
 #pragma unroll
-      for (int u = 0; u < DEC_UNROLL; ++u) {
-        const int key = kk + u * KPI;
+      for (int u = 0; u < UNK; ++u) {
+        const int key = kk + u * KPIK;
 #pragma unroll
         for (int gh = 0; gh < G; ++gh) {
-          const float dot = row_sum<LPK>(dot8(kr[u], qv[gh])) * c;
-          if (col == 0 && key < s1) sc[gh][key - s0] = dot;
+          float part = dot8(kr[u][0], qv[gh][0]);
+#pragma unroll
+          for (int pp = 1; pp < KP; ++pp) part += dot8(kr[u][pp], qv[gh][pp]);
+          const float dot = row_sum<LPKK>(part) * c;
+          if (kcol == 0 && key < s1) sc[gh][key - s0] = dot;
         }
       }
     }
