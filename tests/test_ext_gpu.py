@@ -160,10 +160,12 @@ def test_decode_varlen(Hkv, splits, d, dtype):
         check_max_abs(got_lse[b], lse_ref[b], dtype, f"lse seq {b} (len {n})")
 
 
-@pytest.mark.parametrize("H", [60, 64], ids=["4wave", "8wave"])
-def test_fwd_ex_both_workgroup_shapes(H):
-    """Grouped heads and a window at a grid of 1024 (eight-wave) or 960 (four-wave) blocks."""
-    B, N, d, dtype, window = 4, 1024, 128, torch.bfloat16, 300
+@pytest.mark.parametrize("B,H,N,window", [(4, 60, 1024, 300), (2, 64, 2304, 2100)],
+                         ids=["4wave", "8wave"])
+def test_fwd_ex_both_workgroup_shapes(B, H, N, window):
+    """Grouped heads and a window: windows up to 2048 keys run four-wave workgroups; a
+    2100-key window over 1152 blocks of 256 rows runs eight-wave ones."""
+    d, dtype = 128, torch.bfloat16
     Hkv = H // 4
     seed = 9950 + H
     announce(f"fwd_ex shapes B{B} H{H} Hkv{Hkv} N{N} d{d} window={window} seed={seed}")
@@ -171,7 +173,7 @@ def test_fwd_ex_both_workgroup_shapes(H):
     scale = d ** -0.5
     o, lse = run_fwd_ex(q.to(DEV), k.to(DEV), v.to(DEV), scale, True, window)
     o_h, lse_h = host64(o), host64(lse)
-    for b, h in [(0, 0), (2, H // 2 + 1), (3, H - 1)]:
+    for b, h in [(0, 0), (B // 2, H // 2 + 1), (B - 1, H - 1)]:
         hk = h // (H // Hkv)
         o_ref, lse_ref = oracle.attn_fwd(q[b, h], k[b, hk], v[b, hk], scale, True, window=window)
         check_max_abs(o_h[b, h], o_ref, dtype, f"O head ({b},{h})")
