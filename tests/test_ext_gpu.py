@@ -178,3 +178,25 @@ def test_fwd_ex_both_workgroup_shapes(B, H, N, window):
         o_ref, lse_ref = oracle.attn_fwd(q[b, h], k[b, hk], v[b, hk], scale, True, window=window)
         check_max_abs(o_h[b, h], o_ref, dtype, f"O head ({b},{h})")
         check_max_abs(lse_h[b, h], lse_ref, dtype, f"lse head ({b},{h})")
+
+
+@pytest.mark.parametrize("B,H,N,window", [(4, 60, 1024, 300), (2, 64, 2304, 2100)],
+                         ids=["4wave-dq", "8wave-dq"])
+def test_bwd_ex_both_dq_shapes(B, H, N, window):
+    """Grouped heads and a window in the backward at a dQ grid under (4-wave) and over
+    (8-wave) 1024 blocks of 256 rows; whole key/value groups against the oracle."""
+    d, dtype = 128, torch.bfloat16
+    Hkv = H // 4
+    seed = 9960 + H
+    announce(f"bwd_ex shapes B{B} H{H} Hkv{Hkv} N{N} d{d} window={window} seed={seed}")
+    q, k, v, do = attention_inputs(B, H, N, d, dtype, seed, "cpu", with_dout=True, Hkv=Hkv)
+    scale = d ** -0.5
+    dq, dk, dv = run_bwd_ex(*(t.to(DEV) for t in (q, k, v, do)), scale, True, window)
+    dq_h, dk_h, dv_h = host64(dq), host64(dk), host64(dv)
+    for b, hk in [(0, 0), (B - 1, Hkv - 1)]:
+        hs = slice(4 * hk, 4 * hk + 4)
+        ref = oracle.attn_bwd(q[b, hs], k[b, hk:hk + 1], v[b, hk:hk + 1], do[b, hs], scale, True,
+                              window=window)
+        check_rel_norm(dq_h[b, hs], ref[0], dtype, f"dQ group ({b},{hk})")
+        check_rel_norm(dk_h[b, hk:hk + 1], ref[1], dtype, f"dK head ({b},{hk})")
+        check_rel_norm(dv_h[b, hk:hk + 1], ref[2], dtype, f"dV head ({b},{hk})")
