@@ -29,9 +29,10 @@
  *   - scale must be finite and > 0 (the pages use 1/sqrt(d)).
  *   - Input values must be finite; results for inputs holding NaN or Inf
  *     are unspecified.
- *   - Arithmetic: fp16/bf16 MFMA products with fp32 accumulation; softmax
- *     statistics in fp32; P is rounded to `dt` before the P V product;
- *     outputs are rounded to nearest even.
+ *   - Arithmetic: exact fp16/bf16 products with fp32 accumulation (matrix
+ *     cores in fa_fwd and fa_bwd, packed dot products in fa_decode);
+ *     softmax statistics in fp32; P is rounded to `dt` before the P V
+ *     product; outputs are rounded to nearest even.
  *   - Pointers to fp16/bf16 tensors and workspaces must be 16-byte aligned;
  *     float32 pointers 4-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
