@@ -34,11 +34,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Value held by lane l ^ 32 (the other half of the wave), via v_permlane32_swap.
-__device__ __forceinline__ float other_half(float x) {
+// Max / sum of x over lanes l and l ^ 32 (the two halves of the wave), via
+// v_permlane32_swap on (x, x): afterwards lanes 0-31 hold (own, partner) and
+// lanes 32-63 hold (partner, own), so no lane-dependent select is needed and
+// both lanes of a pair get the same result (max and + are commutative).
+__device__ __forceinline__ float half_pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  // lanes 0-31 receive lane l+32's value in r[1]; lanes 32-63 receive lane l-32's in r[0]
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -111,13 +111,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
       qf[g][kk] = (myq[g] < N) ? ld16<v8>(Qh + (size_t)myq[g] * D + 16 * kk + 8 * hh) : v8{};
 
   f32x16 oacc[QG][D / 32];
-  float m_run[QG], l_run[QG];
+  // m_run: running maximum (log2 units); nref: the negated reference the
+  // probabilities are formed against, -m_run, or -0 while m_run is -inf (a
+  // row that has seen no visible key yet: any finite reference gives its
+  // -inf scores probability 0 rather than NaN).
+  float m_run[QG], l_run[QG], nref[QG];
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[g][i] = f32x16{};
     m_run[g] = -INFINITY;
     l_run[g] = 0.f;
+    nref[g] = -0.f;
   }
 
   const int kv_end = CAUSAL ? min(N, (qb + 1) * BR) : N;
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
           for (int r = 0; r < 16; r += 4)
             mx = fmaxf(fmaxf(mx, sacc[g][sb][r]),
                        fmaxf(fmaxf(sacc[g][sb][r + 1], sacc[g][sb][r + 2]), sacc[g][sb][r + 3]));
-        mx = fmaxf(mx, other_half(mx));
+        mx = half_pair_max(mx);
         const float m_cand = mx * c;
         if (__ballot(m_cand > m_run[g] + FWD_RESCALE_SLACK)) {
           const float m_new = fmaxf(m_run[g], m_cand);
@@ -267,12 +272,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
 #pragma unroll
           for (int nb = 0; nb < D / 32; ++nb) oacc[g][nb] *= alpha;
           m_run[g] = m_new;
+          // (A window can hide every key so far from one row of an active
+          // group, leaving its maximum at -inf.)
+          nref[g] = (m_new == -INFINITY) ? -0.f : -m_new;
         }
-        // A row whose keys so far are all masked (a window can hide a whole
-        // tile from one row of an active group) still has m = -inf: any
-        // finite reference gives its -inf scores probability 0, not NaN.
-        const float mref = (m_run[g] == -INFINITY) ? 0.f : m_run[g];
-        float rs[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial row sums
+        // Four independent partial row sums, started from the first four
+        // probabilities (no additions of zero).
+        float rs[4];
 #pragma unroll
         for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
@@ -280,8 +286,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
             float pv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              pv[e] = fast_exp2(__builtin_fmaf(sacc[g][sb][8 * hf + e], c, -mref));
-              rs[e & 3] += pv[e];
+              pv[e] = fast_exp2(__builtin_fmaf(sacc[g][sb][8 * hf + e], c, nref[g]));
+              rs[e & 3] = (sb == 0 && hf == 0 && e < 4) ? pv[e] : rs[e & 3] + pv[e];
             }
             pb[g][2 * sb + hf] = to_v8<T>(pv);
           }
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   // Epilogue: O = O / l, lse = (m + log2 l) ln 2.
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
-    const float l_tot = l_run[g] + other_half(l_run[g]);
+    const float l_tot = half_pair_sum(l_run[g]);
     const float inv = 1.f / l_tot;
     if (myq[g] < N) {
       T* __restrict__ orow = O + hoff + (size_t)myq[g] * D;
