@@ -196,3 +196,23 @@ def test_binding_rejects_host_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         fa.load_library(str(tmp_path / "libfa.so"))
+
+
+def test_header_is_plain_c_and_callable_from_c(tmp_path):
+    """include/fa.h compiles as strict C99 and the validation paths answer a C caller."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler on this machine")
+    lib_dir = os.path.dirname(fa.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    build = subprocess.run(
+        [cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+         "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c", "abi_from_c.c"),
+         "-L", lib_dir, "-lfa", f"-Wl,-rpath,{lib_dir}", "-o", exe],
+        capture_output=True, text=True)
+    assert build.returncode == 0, build.stdout + build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "0 failure(s)" in run.stdout
