@@ -38,7 +38,7 @@
 //
 // LDS tiles use the forward's unpadded, swizzled layout (fa_tile.h: 16-byte
 // row reads and transpose reads conflict-free) and are filled by direct
-// global-to-LDS loads.
+// buffer-to-LDS loads (TileLoader).
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
     vf[kk] = key_ok ? ld16<v8>(Vh + (size_t)mykey * D + 16 * kk + 8 * hh) : v8{};
-  // Rows past the end are clamped to row N-1; those keys' scores are masked.
-  load_tile<T, D, BK, KV_WAVES>(Kh, Ks, kj0, N, wave, lane);
+  // Rows past the end read as zero; those keys' scores are masked.
+  TileLoader<D, BK, KV_WAVES>(wave, lane).load(Kh, N, kj0, Ks, wave);
 
   f32x16 dvacc[NB], dkacc[NB];
 #pragma unroll
@@ -135,8 +135,8 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   const uint32_t kwb = rb + 64 * D * wave;  // this wave's 32 K rows: 32 D * 2 bytes per wave
 
   // Q and dO tiles of a step go straight into LDS buffer `buf` (rows past the
-  // end clamped to row N-1, their probabilities masked to 0); L and D of the
-  // step's rows go through registers.
+  // end read as zero, their probabilities masked to 0); L and D of the step's
+  // rows go through registers.
   // Steps run over the group's query heads, each over query rows qstart ..
   // qend - 1: causal blocks start at their first key; with a window, queries
   // from the block's last key + window on see none of its keys.
@@ -153,10 +153,11 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     }
   };
   float lpre = 0.f, dpre = 0.f;
+  const TileLoader<D, BQ, KV_WAVES> step_loader(wave, lane);
   auto load_step = [&](int qh, int qi0, int buf) {
     const size_t qoff = (size_t)qh * N * D;
-    load_tile<T, D, BQ, KV_WAVES>(Q + qoff, Qs[buf], qi0, N, wave, lane);
-    load_tile<T, D, BQ, KV_WAVES>(dO + qoff, dOs[buf], qi0, N, wave, lane);
+    step_loader.load(Q + qoff, N, qi0, Qs[buf], wave);
+    step_loader.load(dO + qoff, N, qi0, dOs[buf], wave);
     if (tid < BQ) {
       const int qrow = qi0 + tid;
       lpre = (qrow < N) ? LSE[(size_t)qh * N + qrow] * 1.4426950408889634f : 0.f;
@@ -359,9 +360,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
   // Sliding window: tiles before the block's first visible key are skipped.
   const int kbase = (CAUSAL && window > 0) ? (max(0, qb * BR - window + 1) / BC) * BC : 0;
   const int nt = ntiles - kbase / BC;
-  // Rows past the end of a tile are clamped to row N-1 and masked.
+  // Rows past the end of a tile read as zero and are masked.
+  const TileLoader<D, BC, NW> loader(wave, lane);
   auto load_kv = [&](const T* __restrict__ src, T* dst, int kb) {
-    load_tile<T, D, BC, NW>(src, dst, kb, N, wave, lane);
+    loader.load(src, N, kb, dst, wave);
   };
   // LDS byte offsets by XOR addressing (fa_tile.h): K and V rows (A operands
   // of S^T and dP^T) at row l32, columns 16 kk + 8 hh; K^T (A operand of

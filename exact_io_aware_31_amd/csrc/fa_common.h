@@ -65,11 +65,6 @@ __device__ __forceinline__ void st16(void* p, V v) {
 // ... and additionally until every LDS operation of this wave has completed.
 #define FA_VMCNT_LGKM0(n) (FA_VMCNT(n) & ~(15 << 8))
 
-// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16 l (lds_base must be wave-uniform).
-__device__ __forceinline__ void lds_load16(const void* gptr, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
 // Wait on this wave's outstanding counters.  The empty asm statements with a
 // memory clobber keep the compiler from moving LDS accesses across the wait
 // (the builtin alone is not a memory barrier to the compiler).

@@ -23,11 +23,13 @@
 //     layout with a consistent permutation of the reduction index.  The A
 //     operand V^T is read from the row-major V tile with the LDS transpose
 //     read (ds_read_b64_tr_b16), so V is never transposed in memory.
-//   * K and V tiles reach LDS by direct global-to-LDS loads
-//     (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS
-//     base + 16 * lane) into a ring of tiles: three deep, two tiles ahead of
-//     their use, for eight waves; two deep, one tile ahead, for four (so
-//     that two workgroups fit in LDS).
+//   * K and V tiles reach LDS by direct buffer-to-LDS loads
+//     (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the wave's
+//     LDS base + 16 * lane) into a ring of tiles: three deep, two tiles ahead
+//     of their use, for eight waves; two deep, one tile ahead, for four (so
+//     that two workgroups fit in LDS).  A lane's offset inside a tile is fixed,
+//     so the only per-tile work is a scalar buffer descriptor; its range
+//     check returns zeros for rows past the end.
 //     No registers hold staged data and no LDS store instructions are issued;
 //     each wave waits for its own loads before the tile's barrier.  Tiles are
 //     stored unpadded with 16-byte chunk c of row r at chunk c ^ sw(r), which
@@ -132,11 +134,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   const int kbase = (CAUSAL && window > 0) ? (max(0, qb * BR - window + 1) / BC) * BC : 0;
   const int nt = ntiles - kbase / BC;  // tiles this workgroup streams
 
-  // Tile loads (see load_tile): rows past the end are clamped to row N-1;
-  // those keys are masked to -inf before the softmax, so their probabilities
-  // (and their V rows' weight) are 0.
+  // Tile loads (TileLoader): rows past the end read as zero; those keys are
+  // masked to -inf before the softmax, so their probabilities (and their V
+  // rows' weight) are 0.
+  const TileLoader<D, BC, NW> loader(wave, lane);
   auto load_kv = [&](const T* __restrict__ src, T* dst, int kb) {
-    load_tile<T, D, BC, NW>(src, dst, kb, N, wave, lane);
+    loader.load(src, N, kb, dst, wave);
   };
   // Per-lane element offsets of the operand reads (the swizzle depends on the
   // row mod 16 only, so they hold for every 16- or 32-row block of a tile):

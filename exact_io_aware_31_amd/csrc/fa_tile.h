@@ -65,27 +65,52 @@ __device__ __forceinline__ u32x2 lds_tr_at(const void* tile, uint32_t byte_off) 
   return lds_read_tr16(reinterpret_cast<const char*>(tile) + byte_off);
 }
 
-// Direct global-to-LDS load of rows kb .. kb + BC - 1 of a head into the tile
-// at dst by NW waves: the tile is cut into 1 KiB segments, wave w fills
-// segments w SPW .. w SPW + SPW - 1, and lane l of segment g fills LDS chunk
-// slot l of it, i.e. tile row g RPS + l / (D / 8), physical chunk
-// l mod (D / 8), with the logical chunk the swizzle puts there.  Rows past
-// the end are clamped to row N-1 (callers mask those rows).  Each wave issues
-// SPW loads, counted by its vmcnt.  SW is the tile's chunk swizzle.
-template <typename T, int D, int BC, int NW, typename SW = TileSwizzle<D>>
-__device__ __forceinline__ void load_tile(const T* __restrict__ src, T* dst, int kb, int N,
-                                          int wave, int lane) {
-  constexpr int RPS = 512 / D;             // tile rows per 1 KiB segment
-  constexpr int NSEG = BC * D * 2 / 1024;  // segments per tile
-  constexpr int SPW = NSEG / NW;           // segments each wave loads
-  static_assert(NSEG % NW == 0, "tile segments split evenly over the waves");
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int g = wave * SPW + i;
-    const int row = g * RPS + lane / (D / 8);
-    const int chunk = (lane % (D / 8)) ^ SW::sw(row);
-    lds_load16(src + (size_t)min(kb + row, N - 1) * D + 8 * chunk, dst + g * 512);
-  }
+// Direct buffer load of 16 bytes per lane into LDS: lane l's bytes, read at
+// byte offset voff of a raw buffer of `bytes` bytes starting at base, land at
+// lds_base + 16 l (lds_base wave-uniform).  Offsets at or past `bytes` read
+// as zero.  base and bytes must be wave-uniform (they form the descriptor).
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t bytes, uint32_t voff,
+                                                  void* lds_base) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           voff, 0, 0, 0);
 }
+
+// Direct load of rows kb .. kb + BC - 1 of a head into the tile at dst by NW
+// waves (buffer_load_dwordx4 ... lds): the tile is cut into 1 KiB segments,
+// wave w fills segments w SPW .. w SPW + SPW - 1, and lane l of segment g
+// fills LDS chunk slot l of it, i.e. tile row g RPS + l / (D / 8), physical
+// chunk l mod (D / 8), with the logical chunk the swizzle SW puts there.
+// Each wave issues SPW loads per tile, counted by its vmcnt.  A lane's byte
+// offset inside a tile (its row and swizzled chunk) is the same for every
+// tile, so it is computed once; a tile's position enters only
+// through the buffer descriptor, built in scalar registers per tile: base =
+// the tile's first row, num_records = the bytes from there to the end of the
+// head.  The hardware range check returns zeros for rows past the end (which
+// callers mask), so no clamp is needed and no access can leave the head.
+template <int D, int BC, int NW, typename SW = TileSwizzle<D>>
+struct TileLoader {
+  static constexpr int RPS = 512 / D;
+  static constexpr int NSEG = BC * D * 2 / 1024;
+  static constexpr int SPW = NSEG / NW;
+  static_assert(NSEG % NW == 0, "tile segments split evenly over the waves");
+  uint32_t voff[SPW];
+  __device__ __forceinline__ TileLoader(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int row = (wave * SPW + i) * RPS + lane / (D / 8);
+      voff[i] = 2u * (uint32_t)(row * D + 8 * ((lane % (D / 8)) ^ SW::sw(row)));
+    }
+  }
+  // Rows kb .. kb + BC - 1 of a head of N rows (kb < N) into the tile at dst.
+  template <typename T>
+  __device__ __forceinline__ void load(const T* head, int N, int kb, T* dst, int wave) const {
+    const uint32_t bytes = (uint32_t)(N - kb) * (uint32_t)(D * 2);
+    const void* base = head + (size_t)kb * D;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) buffer_load_lds16(base, bytes, voff[i], dst + (wave * SPW + i) * 512);
+  }
+};
 
 }  // namespace fa
