@@ -88,10 +88,8 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
   // Work item: XCD-local heads; causal key blocks heaviest (first) first.
-  const int p = blockIdx.x;
-  const int w = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
-  const int kvbh = w / nkb;  // key/value head (over B x H_kv)
-  const int kblk = w % nkb;
+  int kvbh, kblk;  // key/value head (over B x H_kv), key block
+  work_item(blockIdx.x, total / nkb, nkb, kvbh, kblk);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform_int(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
@@ -322,10 +320,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) T V0[BC * D], V1[BC * D], V2[RING > 2 ? BC * D : 1];
 
   // Work item: XCD-local heads, heaviest causal query blocks first.
-  const int p = blockIdx.x;
-  const int w = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
-  const int bh = w / nqb;
-  const int qb = CAUSAL ? nqb - 1 - (w % nqb) : (w % nqb);
+  int bh, rank;
+  work_item(blockIdx.x, total / nqb, nqb, bh, rank);
+  const int qb = CAUSAL ? nqb - 1 - rank : rank;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform_int(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;

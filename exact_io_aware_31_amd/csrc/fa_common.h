@@ -85,6 +85,27 @@ __device__ __forceinline__ void bare_barrier() {
 }
 __device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Work item of workgroup p in a grid of nheads x nblk items, where block rank
+// 0 of a head is its heaviest.  The hardware deals workgroups round-robin
+// over the 8 XCDs (p mod 8).  When the heads split evenly over the XCDs, each
+// XCD gets its own heads (so their K and V stay in its L2) and runs their
+// blocks rank-major: every head's heaviest block first, then every head's
+// next one, so the lightest blocks of all its heads fill the end (a head-major
+// order leaves heavy blocks of the last heads starting late).  Otherwise the
+// XCD-contiguous head-major order, or plain order, is used.
+__device__ __forceinline__ void work_item(int p, int nheads, int nblk, int& head, int& rank) {
+  if (nheads % 8 == 0) {
+    const int hpx = nheads / 8, local = p / 8;
+    head = (p % 8) * hpx + local % hpx;
+    rank = local / hpx;
+  } else {
+    const int total = nheads * nblk;
+    const int w = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
+    head = w / nblk;
+    rank = w % nblk;
+  }
+}
+
 // Round 8 floats to the storage type (round to nearest even).
 template <typename T>
 __device__ __forceinline__ typename Vec<T>::v8 to_v8(const float* x) {
