@@ -89,7 +89,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
 
   // Work item: XCD-local heads; causal key blocks heaviest (first) first.
   int kvbh, kblk;  // key/value head (over B x H_kv), key block
-  work_item(blockIdx.x, total / nkb, nkb, kvbh, kblk);
+  work_item(blockIdx.x, total / nkb, nkb, CAUSAL && !WIN, kvbh, kblk);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform_int(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
 
   // Work item: XCD-local heads, heaviest causal query blocks first.
   int bh, rank;
-  work_item(blockIdx.x, total / nqb, nqb, bh, rank);
+  work_item(blockIdx.x, total / nqb, nqb, CAUSAL && !WIN, bh, rank);
   const int qb = CAUSAL ? nqb - 1 - rank : rank;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform_int(tid >> 6);  // wave-uniform

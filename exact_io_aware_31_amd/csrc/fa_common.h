@@ -87,14 +87,16 @@ __device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_read
 
 // Work item of workgroup p in a grid of nheads x nblk items, where block rank
 // 0 of a head is its heaviest.  The hardware deals workgroups round-robin
-// over the 8 XCDs (p mod 8).  When the heads split evenly over the XCDs, each
-// XCD gets its own heads (so their K and V stay in its L2) and runs their
-// blocks rank-major: every head's heaviest block first, then every head's
-// next one, so the lightest blocks of all its heads fill the end (a head-major
-// order leaves heavy blocks of the last heads starting late).  Otherwise the
-// XCD-contiguous head-major order, or plain order, is used.
-__device__ __forceinline__ void work_item(int p, int nheads, int nblk, int& head, int& rank) {
-  if (nheads % 8 == 0) {
+// over the 8 XCDs (p mod 8); each XCD gets its own heads (so their K and V
+// are read through its L2).  With uneven blocks (causal, no window) and heads
+// that split evenly over the XCDs, an XCD runs its heads' blocks rank-major:
+// every head's heaviest block first, then every head's next one, so the
+// lightest blocks of all its heads fill the end (head-major leaves heavy
+// blocks of the last heads starting late).  Otherwise it runs them
+// head-major, which keeps fewer heads' K and V in its L2 at a time.
+__device__ __forceinline__ void work_item(int p, int nheads, int nblk, bool uneven, int& head,
+                                          int& rank) {
+  if (uneven && nheads % 8 == 0) {
     const int hpx = nheads / 8, local = p / 8;
     head = (p % 8) * hpx + local % hpx;
     rank = local / hpx;

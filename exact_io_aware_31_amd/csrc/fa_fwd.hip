@@ -84,7 +84,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
 
   // Work item: XCD-local heads, heaviest causal query blocks first.
   int bh, rank;
-  work_item(blockIdx.x, total / nqb, nqb, bh, rank);
+  work_item(blockIdx.x, total / nqb, nqb, CAUSAL && !WIN, bh, rank);
   const int qb = CAUSAL ? nqb - 1 - rank : rank;
 
   const int tid = threadIdx.x, lane = tid & 63;
