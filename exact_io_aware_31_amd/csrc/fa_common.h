@@ -87,13 +87,17 @@ __device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_read
 
 // Work item of workgroup p in a grid of nheads x nblk items, where block rank
 // 0 of a head is its heaviest.  The hardware deals workgroups round-robin
-// over the 8 XCDs (p mod 8); each XCD gets its own heads (so their K and V
-// are read through its L2).  With uneven blocks (causal, no window) and heads
-// that split evenly over the XCDs, an XCD runs its heads' blocks rank-major:
-// every head's heaviest block first, then every head's next one, so the
-// lightest blocks of all its heads fill the end (head-major leaves heavy
-// blocks of the last heads starting late).  Otherwise it runs them
-// head-major, which keeps fewer heads' K and V in its L2 at a time.
+// over the 8 XCDs (p mod 8), and items are mapped so that each XCD works on
+// its own heads (their K and V are read through its L2):
+//   * uneven blocks (causal, no window) and heads that split evenly over the
+//     XCDs: an XCD runs its heads' blocks rank-major, every head's heaviest
+//     block first, then every head's next one, so the lightest blocks of all
+//     its heads fill the end (head-major leaves heavy blocks of the last
+//     heads starting late);
+//   * otherwise, when the grid splits evenly over the XCDs: head-major over
+//     a contiguous range of items per XCD, which keeps fewer heads' K and V
+//     in its L2 at a time;
+//   * else items in plain order.
 __device__ __forceinline__ void work_item(int p, int nheads, int nblk, bool uneven, int& head,
                                           int& rank) {
   if (uneven && nheads % 8 == 0) {
