@@ -7,7 +7,9 @@ packed-fp32 instruction selection disabled (``-packed-fp32-ops``) and with
 ``-fno-honor-nans``: the library's contract requires finite inputs, which
 lets max reductions compile to bare v_max/v_max3 without NaN-quieting
 canonicalisations.
-Output: exact_io_aware_31_amd/_lib/libfa.so.
+Output: exact_io_aware_31_amd/_lib/libfa.so (the attention library) and
+exact_io_aware_31_amd/_lib/libfa_probe.so (the two measurement kernels of
+include/fa_probe.h, used by the benchmark to measure the chip's own ceilings).
 """
 import concurrent.futures as cf
 import os
@@ -20,8 +22,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libfa.so")
+PROBE_LIB = os.path.join(LIB_DIR, "libfa_probe.so")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
+PROBE_SOURCES = ["fa_probe_api.cpp", "fa_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -55,18 +59,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     _check_kernel_stubs(tmp)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile and link libfa.so and libfa_probe.so; returns the path of libfa.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 
@@ -83,7 +93,8 @@ def _check_kernel_stubs(lib: str) -> None:
         return  # no nm available: skip the check rather than fail the build
     missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
     if missing:
-        raise RuntimeError("kernel launch stubs missing from libfa.so: " + ", ".join(missing))
+        raise RuntimeError(f"kernel launch stubs missing from {os.path.basename(lib)}: "
+                           + ", ".join(missing))
 
 
 if __name__ == "__main__":

@@ -43,17 +43,25 @@ fa_status check_ext(int H, int H_kv, int window, int causal) {
   return FA_OK;
 }
 
-// Shared body of fa_decode_ex and fa_decode_varlen (kv_lens may be null).
-fa_status decode_impl(const void* q, const void* k, const void* v, const int* kv_lens, void* o,
-                      float* lse, int B, int H, int H_kv, int Nkv, int d, float scale,
-                      int num_splits, void* workspace, size_t workspace_bytes, fa_dtype dt,
-                      void* stream) {
+// Checks shared by every decode entry point, apart from the workspace.
+fa_status check_decode(const void* q, const void* k, const void* v, void* o, int B, int H,
+                       int H_kv, int Nkv, int d, float scale, int num_splits, fa_dtype dt) {
   if (!q || !k || !v || !o) return FA_ERR_NULL;
   fa_status st = check_common(B, H, Nkv, d, scale, dt);
   if (st != FA_OK) return st;
   if ((st = check_ext(H, H_kv, 0, 0)) != FA_OK) return st;
   if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
   if ((long long)B * H * num_splits > kMaxGrid) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// Shared body of fa_decode_ex and fa_decode_varlen (kv_lens may be null).
+fa_status decode_impl(const void* q, const void* k, const void* v, const int* kv_lens, void* o,
+                      float* lse, int B, int H, int H_kv, int Nkv, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes, fa_dtype dt,
+                      void* stream) {
+  fa_status st = check_decode(q, k, v, o, B, H, H_kv, Nkv, d, scale, num_splits, dt);
+  if (st != FA_OK) return st;
   if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits))
     return FA_ERR_WORKSPACE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||

@@ -501,9 +501,9 @@ template <typename T, int D, bool CAUSAL, bool WIN>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.H * a.N;
   const long pre_threads = rows * (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((pre_threads + 255) / 256)), dim3(256),
-                     0, s, static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.drow, rows);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_kernel(bwd_pre_kernel<T, D>, dim3((unsigned)((pre_threads + 255) / 256)),
+                               dim3(256), s, static_cast<const T*>(a.o),
+                               static_cast<const T*>(a.dout), a.drow, rows);
   if (e != hipSuccess) return e;
   const float c = a.scale * 1.4426950408889634f;
   const T* q = static_cast<const T*>(a.q);
@@ -515,10 +515,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int window = WIN ? a.window : 0;
   const int nkb = (a.N + KV_BK - 1) / KV_BK;
   const int kv_total = a.B * a.Hkv * nkb;
-  hipLaunchKernelGGL((bwd_kv_kernel<T, D, CAUSAL, WIN>), dim3(kv_total), dim3(KV_WAVES * 64), 0, s, q, k,
-                     v, dout, a.lse, a.drow, static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, nkb,
-                     kv_total, group, window, a.scale, c);
-  e = hipGetLastError();
+  e = launch_kernel(bwd_kv_kernel<T, D, CAUSAL, WIN>, dim3(kv_total), dim3(KV_WAVES * 64), s, q, k,
+                    v, dout, a.lse, a.drow, static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, nkb,
+                    kv_total, group, window, a.scale, c);
   if (e != hipSuccess) return e;
 
   // dQ: fewer 256-row blocks than CUs: four-wave workgroups, two per CU.
@@ -529,14 +528,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int nqb = (a.N + br - 1) / br;
   const int dq_total = a.B * a.H * nqb;
   if (small)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, WIN, 4>), dim3(dq_total), dim3(4 * 64), 0, s, q,
-                       k, v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
+    return launch_kernel(bwd_dq_kernel<T, D, CAUSAL, WIN, 4>, dim3(dq_total), dim3(4 * 64), s, q, k,
+                         v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
+                         window, a.scale, c);
+  return launch_kernel(bwd_dq_kernel<T, D, CAUSAL, WIN, 8>, dim3(dq_total), dim3(8 * 64), s, q, k, v,
+                       dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
                        window, a.scale, c);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, WIN, 8>), dim3(dq_total), dim3(8 * 64), 0, s, q,
-                       k, v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
-                       window, a.scale, c);
-  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -553,7 +550,5 @@ static hipError_t launch_bwd_dt(const BwdArgs& a, hipStream_t s) {
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   return a.dt == DType::BF16 ? launch_bwd_dt<__bf16>(a, s) : launch_bwd_dt<_Float16>(a, s);
 }
-
-size_t bwd_drow_bytes(int B, int H, int N) { return align256((size_t)B * H * N * sizeof(float)); }
 
 }  // namespace fa

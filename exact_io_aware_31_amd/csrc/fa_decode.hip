@@ -324,11 +324,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
 template <typename T, int D, int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
   const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(a.B * a.H / G * a.splits),
-                     dim3(DEC_THREADS), 0, s, static_cast<const T*>(a.q),
-                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.kv_lens, a.part_o,
-                     a.part_lse, a.Nkv, a.splits, a.Hkv, a.H / a.Hkv, c);
-  return hipGetLastError();
+  return launch_kernel(decode_split_kernel<T, D, G>, dim3(a.B * a.H / G * a.splits),
+                       dim3(DEC_THREADS), s, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.kv_lens, a.part_o,
+                       a.part_lse, a.Nkv, a.splits, a.Hkv, a.H / a.Hkv, c);
 }
 
 template <typename T, int D>
@@ -341,9 +340,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
                  : (group % 2 == 0) ? launch_decode_g<T, D, 2>(a, s)
                                     : launch_decode_g<T, D, 1>(a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.B * a.H), dim3(64), 0, s, a.part_o,
-                     a.part_lse, static_cast<T*>(a.o), a.lse, a.splits);
-  return hipGetLastError();
+  return launch_kernel(decode_merge_kernel<T, D>, dim3(a.B * a.H), dim3(64), s, a.part_o,
+                       a.part_lse, static_cast<T*>(a.o), a.lse, a.splits);
 }
 
 template <typename T>
@@ -353,13 +351,6 @@ static hipError_t launch_decode_dt(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   return a.dt == DType::BF16 ? launch_decode_dt<__bf16>(a, s) : launch_decode_dt<_Float16>(a, s);
-}
-
-size_t decode_part_o_bytes(int B, int H, int d, int splits) {
-  return align256((size_t)B * H * splits * d * sizeof(float));
-}
-size_t decode_part_lse_bytes(int B, int H, int splits) {
-  return align256((size_t)B * H * splits * sizeof(float));
 }
 
 }  // namespace fa

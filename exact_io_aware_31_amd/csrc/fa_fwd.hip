@@ -359,11 +359,10 @@ static hipError_t launch_fwd_nw(const FwdArgs& a, hipStream_t s) {
   const int nqb = (a.N + br - 1) / br;
   const int total = a.B * a.H * nqb;
   const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, WIN, NW, FWD_QG>), dim3(total), dim3(NW * 64), 0, s,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.N, nqb, total,
-                     a.H / a.Hkv, WIN ? a.window : 0, c);
-  return hipGetLastError();
+  return launch_kernel(fwd_kernel<T, D, CAUSAL, WIN, NW, FWD_QG>, dim3(total), dim3(NW * 64), s,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.N, nqb, total,
+                       a.H / a.Hkv, WIN ? a.window : 0, c);
 }
 
 // Fewer than four 256-row blocks per CU (1024 on the 256 CUs): four-wave

@@ -5,7 +5,29 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <tuple>
+#include <utility>
+
 namespace fa {
+
+// Launch `kernel` on stream s and return the runtime's verdict on this launch
+// alone.  hipLaunchKernel reports the launch's own error; reading it back
+// with hipGetLastError() after a triple-chevron launch would also return
+// (and clear) an error an earlier, unrelated call of the same thread left.
+// The arguments are converted to the kernel's parameter types first.
+template <typename... Params, size_t... I>
+hipError_t launch_packed(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s,
+                         std::tuple<Params...>& p, std::index_sequence<I...>) {
+  void* ptrs[] = {static_cast<void*>(&std::get<I>(p))..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, s);
+}
+template <typename... Params, typename... Args>
+hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s,
+                         Args&&... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  std::tuple<Params...> p(std::forward<Args>(args)...);
+  return launch_packed(kernel, grid, block, s, p, std::index_sequence_for<Params...>{});
+}
 
 enum class DType { F16 = 0, BF16 = 1 };
 
@@ -49,11 +71,19 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
-// Workspace layouts (bytes), shared by the size queries and the launchers.
-size_t bwd_drow_bytes(int B, int H, int N);
-size_t decode_part_o_bytes(int B, int H, int d, int splits);
-size_t decode_part_lse_bytes(int B, int H, int splits);
-
+// Workspace layouts (bytes), shared by the size queries and the launchers:
+// the backward's float32 row terms D [B, H, N]; the decode's float32 partial
+// outputs [B, H, splits, d], then partial log-sum-exps [B, H, splits]; each
+// part rounded up to 256 bytes.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t bwd_drow_bytes(int B, int H, int N) {
+  return align256((size_t)B * H * N * sizeof(float));
+}
+inline size_t decode_part_o_bytes(int B, int H, int d, int splits) {
+  return align256((size_t)B * H * splits * d * sizeof(float));
+}
+inline size_t decode_part_lse_bytes(int B, int H, int splits) {
+  return align256((size_t)B * H * splits * sizeof(float));
+}
 
 }  // namespace fa

@@ -42,9 +42,14 @@
  *     workspaces sized by the *_workspace_bytes queries.  The library never
  *     allocates or frees device memory and keeps no state between calls.
  *     Outputs must not alias inputs.
- *   - Errors: every argument is validated before any HIP call; on error
- *     nothing is enqueued and no output is touched.  No C++ exception
- *     crosses this interface.
+ *   - Errors: every argument is validated before any HIP call; on a
+ *     validation error (every code but FA_ERR_HIP) nothing is enqueued and
+ *     no output is touched.  FA_ERR_HIP means the runtime refused a kernel
+ *     launch (each launch's own error code is checked, so an error an
+ *     earlier, unrelated HIP call left behind is not reported here).  A call
+ *     that launches several kernels may have enqueued the earlier ones when a
+ *     later launch is refused, so after FA_ERR_HIP the outputs and the
+ *     workspace are undefined.  No C++ exception crosses this interface.
  */
 #ifndef FA_H_
 #define FA_H_

@@ -345,18 +345,25 @@ int oracle_lse_merge(const double* o_parts, const double* lse_parts, long nparts
  *   dK = scale * dS^T Q
  * Masked entries have P = 0 and so contribute nothing.  P is rebuilt here
  * from the definition in float64 (it does not use any saved statistic).
- * Scratch: two n x n double matrices per head.
+ * Scratch: two n x n double matrices per head.  Returns 0, or 2 if a
+ * thread's row buffer could not be allocated (outputs then undefined).
  */
-static void oracle_bwd_head(const double* q, const double* k, const double* v,
+static int oracle_bwd_head(const double* q, const double* k, const double* v,
                             const double* dout, double* dq, double* dk, double* dv,
                             double* drow, long n, long d, double scale, int causal, long window,
                             double* P, double* dS) {
+  int failed = 0;
   /* rebuild P row by row from its definition */
 #pragma omp parallel
   {
-    double* srow = (double*)malloc(sizeof(double) * (size_t)n);
+    double* srow = (double*)malloc(sizeof(double) * (size_t)n + 8);
+    if (!srow) {
+#pragma omp atomic write
+      failed = 1;
+    }
 #pragma omp for schedule(dynamic, 16)
     for (long i = 0; i < n; ++i) {
+      if (!srow) continue;
       for (long j = 0; j < n; ++j) {
         if (!oracle_visible(i, j, causal, window)) { srow[j] = -INFINITY; continue; }
         double acc = 0.0;
@@ -367,6 +374,7 @@ static void oracle_bwd_head(const double* q, const double* k, const double* v,
     }
     free(srow);
   }
+  if (failed) return 2;
   /* dP = dO V^T, D_i = sum_j P_ij dP_ij, dS = P o (dP - D) */
 #pragma omp parallel for schedule(dynamic, 16)
   for (long i = 0; i < n; ++i) {
@@ -406,6 +414,7 @@ static void oracle_bwd_head(const double* q, const double* k, const double* v,
     }
     for (long c = 0; c < d; ++c) dk[j * d + c] *= scale;
   }
+  return 0;
 }
 
 /*
@@ -435,8 +444,12 @@ int oracle_attn_bwd_w(const double* q, const double* k, const double* v,
     for (long h = 0; h < H; ++h) {
       size_t qoff = (size_t)(b * H + h) * n * d;
       size_t kvoff = (size_t)(b * Hkv + h / (H / Hkv)) * n * d;
-      oracle_bwd_head(q + qoff, k + kvoff, v + kvoff, dout + qoff, dq + qoff, gk, gv,
-                      drow ? drow + (b * H + h) * n : NULL, n, d, scale, causal, window, P, dS);
+      if (oracle_bwd_head(q + qoff, k + kvoff, v + kvoff, dout + qoff, dq + qoff, gk, gv,
+                          drow ? drow + (b * H + h) * n : NULL, n, d, scale, causal, window, P,
+                          dS) != 0) {
+        free(P); free(dS); free(gk); free(gv);
+        return 2;
+      }
       for (long e = 0; e < n * d; ++e) {
         dk[kvoff + e] += gk[e];
         dv[kvoff + e] += gv[e];

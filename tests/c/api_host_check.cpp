@@ -1,0 +1,158 @@
+// A host-only check of the C ABI layer (exact_io_aware_31_amd/csrc/fa_api.cpp), built by the
+// CPU test suite with AddressSanitizer and UndefinedBehaviorSanitizer.
+//
+// The kernel launchers are replaced here by stand-ins that record the arguments the ABI layer
+// hands them and enqueue nothing, so the whole layer -- validation, workspace carving, the
+// window and grouped-head normalisation -- runs on a machine without a GPU.  Every call with
+// invalid arguments must fail with the documented status before reaching a launcher; every
+// valid call must reach exactly one launcher with the arguments the header describes.  Prints one line per check; exits non-zero on any failure.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+int g_calls = 0;
+fa::FwdArgs g_fwd;
+fa::BwdArgs g_bwd;
+fa::DecodeArgs g_dec;
+hipStream_t g_stream = nullptr;
+}  // namespace
+
+namespace fa {
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
+  ++g_calls;
+  g_fwd = a;
+  g_stream = s;
+  return hipSuccess;
+}
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
+  ++g_calls;
+  g_bwd = a;
+  g_stream = s;
+  return hipSuccess;
+}
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  ++g_calls;
+  g_dec = a;
+  g_stream = s;
+  return hipSuccess;
+}
+}  // namespace fa
+
+static int failures = 0;
+
+static void check(const char* what, bool ok) {
+  printf("%s %s\n", ok ? "ok  " : "FAIL", what);
+  if (!ok) ++failures;
+}
+
+static void expect(const char* what, fa_status got, fa_status want, int launches_before) {
+  const bool ok = got == want && (want != FA_OK ? g_calls == launches_before
+                                                : g_calls == launches_before + 1);
+  printf("%s %s: got %s, want %s\n", ok ? "ok  " : "FAIL", what, fa_status_string(got),
+         fa_status_string(want));
+  if (!ok) ++failures;
+}
+
+int main() {
+  // Stand-in device addresses: suitably aligned, never dereferenced by the layer.
+  void* q = (void*)(uintptr_t)0x100000;
+  void* k = (void*)(uintptr_t)0x200000;
+  void* v = (void*)(uintptr_t)0x300000;
+  void* o = (void*)(uintptr_t)0x400000;
+  float* lse = (float*)(uintptr_t)0x500000;
+  void* dout = (void*)(uintptr_t)0x600000;
+  void* dq = (void*)(uintptr_t)0x700000;
+  void* dk = (void*)(uintptr_t)0x800000;
+  void* dv = (void*)(uintptr_t)0x900000;
+  char* ws = (char*)(uintptr_t)0xa00000;
+  void* odd = (void*)(uintptr_t)0x100002;
+  void* stream = (void*)(uintptr_t)0x1234;
+  int n;
+
+  // forward
+  n = g_calls;
+  expect("fwd valid", fa_fwd(q, k, v, o, lse, 2, 3, 100, 64, 0.125f, 1, FA_BF16, stream), FA_OK, n);
+  check("fwd forwards its arguments",
+        g_fwd.q == q && g_fwd.k == k && g_fwd.v == v && g_fwd.o == o && g_fwd.lse == lse &&
+            g_fwd.B == 2 && g_fwd.H == 3 && g_fwd.Hkv == 3 && g_fwd.N == 100 && g_fwd.d == 64 &&
+            g_fwd.window == 0 && g_fwd.causal && g_fwd.dt == fa::DType::BF16 &&
+            g_fwd.scale == 0.125f && g_stream == (hipStream_t)stream);
+  n = g_calls;
+  expect("fwd_ex window >= N is no window",
+         fa_fwd_ex(q, k, v, o, lse, 1, 8, 2, 64, 128, 0.1f, 1, 64, FA_F16, nullptr), FA_OK, n);
+  check("fwd_ex forwards H_kv and clears the window", g_fwd.Hkv == 2 && g_fwd.window == 0 &&
+                                                         g_fwd.dt == fa::DType::F16);
+  n = g_calls;
+  expect("fwd_ex window 17", fa_fwd_ex(q, k, v, o, lse, 1, 8, 2, 64, 128, 0.1f, 1, 17, FA_F16,
+                                       nullptr), FA_OK, n);
+  check("fwd_ex keeps a window below N", g_fwd.window == 17);
+  n = g_calls;
+  expect("fwd null lse", fa_fwd(q, k, v, o, nullptr, 1, 1, 16, 64, 0.1f, 0, FA_BF16, nullptr),
+         FA_ERR_NULL, n);
+  expect("fwd scale 0", fa_fwd(q, k, v, o, lse, 1, 1, 16, 64, 0.0f, 0, FA_BF16, nullptr),
+         FA_ERR_SHAPE, n);
+  expect("fwd scale NaN",
+         fa_fwd(q, k, v, o, lse, 1, 1, 16, 64, __builtin_nanf(""), 0, FA_BF16, nullptr),
+         FA_ERR_SHAPE, n);
+  expect("fwd N*d at 2^31", fa_fwd(q, k, v, o, lse, 1, 1, 1 << 24, 128, 0.1f, 0, FA_BF16, nullptr),
+         FA_ERR_SHAPE, n);
+  expect("fwd B*H overflow", fa_fwd(q, k, v, o, lse, 1 << 20, 1 << 20, 64, 64, 0.1f, 0, FA_BF16,
+                                    nullptr), FA_ERR_SHAPE, n);
+  expect("fwd misaligned q", fa_fwd(odd, k, v, o, lse, 1, 1, 16, 64, 0.1f, 0, FA_BF16, nullptr),
+         FA_ERR_ALIGN, n);
+
+  // backward
+  const size_t bws = fa_bwd_workspace_bytes(2, 4, 300, 128);
+  check("bwd workspace = 4 B per row, 256-byte rounded", bws == ((2 * 4 * 300 * 4 + 255) & ~255u));
+  n = g_calls;
+  expect("bwd valid", fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, bws, 2, 4, 300, 128, 0.1f, 1,
+                             FA_BF16, nullptr), FA_OK, n);
+  check("bwd forwards its arguments and the row-term workspace",
+        g_bwd.drow == (float*)ws && g_bwd.dq == dq && g_bwd.dk == dk && g_bwd.dv == dv &&
+            g_bwd.dout == dout && g_bwd.N == 300 && g_bwd.Hkv == 4 && g_bwd.window == 0);
+  n = g_calls;
+  expect("bwd workspace one byte short", fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, bws - 1, 2,
+                                                4, 300, 128, 0.1f, 1, FA_BF16, nullptr),
+         FA_ERR_WORKSPACE, n);
+  expect("bwd_ex window without causal",
+         fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, ws, bws, 2, 4, 2, 300, 128, 0.1f, 0, 5,
+                   FA_BF16, nullptr), FA_ERR_UNSUPPORTED, n);
+  expect("bwd_ex negative window",
+         fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, ws, bws, 2, 4, 2, 300, 128, 0.1f, 1, -1,
+                   FA_BF16, nullptr), FA_ERR_SHAPE, n);
+  expect("bwd null dv", fa_bwd(q, k, v, o, lse, dout, dq, dk, nullptr, ws, bws, 2, 4, 300, 128,
+                               0.1f, 1, FA_BF16, nullptr), FA_ERR_NULL, n);
+
+  // decode: the workspace is carved into partial outputs, then partial log-sum-exps
+  const size_t dws = fa_decode_workspace_bytes(3, 8, 64, 5);
+  const size_t po = ((size_t)3 * 8 * 5 * 64 * 4 + 255) & ~(size_t)255;
+  check("decode workspace = partial outputs + partial lse",
+        dws == po + (((size_t)3 * 8 * 5 * 4 + 255) & ~(size_t)255));
+  n = g_calls;
+  expect("decode_ex valid", fa_decode_ex(q, k, v, o, nullptr, 3, 8, 4, 1000, 64, 0.1f, 5, ws, dws,
+                                         FA_F16, nullptr), FA_OK, n);
+  check("decode carves the workspace",
+        g_dec.part_o == (float*)ws && g_dec.part_lse == (float*)(ws + po) && g_dec.lse == nullptr &&
+            g_dec.splits == 5 && g_dec.Hkv == 4 && g_dec.kv_lens == nullptr && g_dec.Nkv == 1000);
+  n = g_calls;
+  const int* lens = (const int*)(uintptr_t)0xb00000;
+  expect("decode_varlen valid", fa_decode_varlen(q, k, v, lens, o, lse, 3, 8, 4, 1000, 64, 0.1f,
+                                                 5, ws, dws, FA_F16, nullptr), FA_OK, n);
+  check("decode_varlen forwards the lengths", g_dec.kv_lens == lens);
+  n = g_calls;
+  expect("decode splits above the maximum",
+         fa_decode(q, k, v, o, lse, 3, 8, 1000, 64, 0.1f, FA_MAX_SPLITS + 1, ws, 1 << 30, FA_F16,
+                   nullptr), FA_ERR_SPLITS, n);
+  expect("decode_varlen misaligned lengths",
+         fa_decode_varlen(q, k, v, (const int*)odd, o, lse, 3, 8, 4, 1000, 64, 0.1f, 5, ws, dws,
+                          FA_F16, nullptr), FA_ERR_ALIGN, n);
+
+  for (int s = -1; s <= 10; ++s) check("status string", fa_status_string((fa_status)s) != nullptr &&
+                                                            strlen(fa_status_string((fa_status)s)) > 0);
+  printf("%d failure(s)\n", failures);
+  return failures != 0;
+}

@@ -12,6 +12,9 @@ Tolerances (max-abs for outputs, relative Frobenius norm for gradients):
     of the cancelling terms is about 1e-7 per element.
 Each failure message also reports the storage-type rounding floor
 max|round(ref) - ref|, the error a perfectly rounded result would have.
+check_rel_norm_blocks applies the gradient bound to every block of 32 rows
+separately (one row block of a wave), so that a wrong row or block, which
+barely moves a whole-tensor norm, still fails.
 """
 import sys
 
@@ -61,3 +64,22 @@ def check_rel_norm(got: np.ndarray, ref: np.ndarray, dtype, what: str) -> float:
 
 def nan_like(t: torch.Tensor) -> torch.Tensor:
     return torch.full_like(t, float("nan"))
+
+
+def check_rel_norm_blocks(got: np.ndarray, ref: np.ndarray, dtype, what: str,
+                          rows: int = 32) -> float:
+    """The gradient bound of check_rel_norm on every block of `rows` rows (axis -2)."""
+    tol = TOL_GRAD[dtype]
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    n = ref.shape[-2]
+    worst = 0.0
+    for r0 in range(0, n, rows):
+        g, r = got[..., r0:r0 + rows, :], ref[..., r0:r0 + rows, :]
+        den = float(np.linalg.norm(r))
+        diff = float(np.linalg.norm(g - r))
+        assert diff <= tol * den + GRAD_ATOL_RMS * np.sqrt(r.size), (
+            f"{what}: rows {r0}..{r0 + r.shape[-2] - 1}: relative norm error "
+            f"{diff / max(den, 1e-30):.4e} > {tol:.1e} (||ref|| = {den:.3e})")
+        worst = max(worst, diff / max(den, 1e-30))
+    return worst

@@ -36,8 +36,8 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_decode", "fa_fwd_ex", "fa_bwd_ex",
-                          "fa_decode_ex", "fa_decode_varlen", "fa_bwd_workspace_bytes",
-                          "fa_decode_workspace_bytes",
+                          "fa_decode_ex", "fa_decode_varlen",
+                          "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/fa.h but not exported"
@@ -172,6 +172,22 @@ def test_decode_varlen_validation(lib):
     assert call(H_kv=3) == ERR["FA_ERR_SHAPE"]
     assert call(splits=0) == ERR["FA_ERR_SPLITS"]
     assert call(d=32) == ERR["FA_ERR_UNSUPPORTED"]
+
+
+def test_probe_library_exports_every_declared_function():
+    from exact_io_aware_31_amd import probe
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "fa_probe.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(fa_probe_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["fa_probe_mfma_bf16", "fa_probe_stream_read"]
+    plib = probe.load_library()
+    for n in names:
+        assert hasattr(plib, n), f"{n} declared in include/fa_probe.h but not exported"
+    # argument checks happen before any launch
+    assert plib.fa_probe_mfma_bf16(NULL, P, 1, 1, NULL) == 1
+    assert plib.fa_probe_mfma_bf16(P, P, 0, 1, NULL) == 2
+    assert plib.fa_probe_stream_read(P, probe.READ_CHUNK + 16, P, 1, NULL) == 2
+    assert plib.fa_probe_stream_read(P_ODD, probe.READ_CHUNK, P, 1, NULL) == 4
 
 
 def test_bwd_ex_workspace_is_per_query_head(lib):

@@ -11,7 +11,7 @@ import torch
 import exact_io_aware_31_amd as fa
 import oracle
 from synth_inputs import BWD_4K, attention_inputs
-from tests.parity_util import announce, check_rel_norm, host64, nan_like
+from tests.parity_util import announce, check_rel_norm, check_rel_norm_blocks, host64, nan_like
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -58,6 +58,7 @@ def test_bwd_full_size_workload():
         ref = oracle.attn_bwd(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
         for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
             check_rel_norm(host64(g[b, h]), r, w.dtype, f"{name} head ({b},{h})")
+            check_rel_norm_blocks(host64(g[b, h]), r, w.dtype, f"{name} head ({b},{h})")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
@@ -76,6 +77,7 @@ def test_bwd_many_heads(causal, d, dtype):
         ref = oracle.attn_bwd(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
         for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
             check_rel_norm(host64(g[b, h]), r, dtype, f"{name} head ({b},{h})")
+            check_rel_norm_blocks(host64(g[b, h]), r, dtype, f"{name} head ({b},{h})")
 
 
 def test_bwd_at_bench_shape():
@@ -89,6 +91,7 @@ def test_bwd_at_bench_shape():
         ref = oracle.attn_bwd(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
         for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
             check_rel_norm(host64(g[b, h]), r, w.dtype, f"{name} head ({b},{h})")
+            check_rel_norm_blocks(host64(g[b, h]), r, w.dtype, f"{name} head ({b},{h})")
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
