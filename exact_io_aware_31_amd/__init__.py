@@ -11,6 +11,9 @@ Low-level functions carry the C names and take caller-allocated tensors:
     fa_decode(q, k, v, o, lse, scale, num_splits, workspace)
     fa_decode_varlen(q, k, v, kv_lens, o, lse, scale, num_splits, workspace): decode
         over a padded cache of ragged per-sequence histories
+    fa_decode_noalloc(q, k, v, o, lse, scale, num_splits): fa_decode_ex without a
+        workspace argument (the library's static device scratch instead), for
+        callers that cannot allocate
     fa_fwd_ex / fa_bwd_ex / fa_decode_ex: the same with grouped key/value heads
         (k, v with H_kv heads dividing H) and, forward and backward, a causal
         sliding window (window=w: key j visible to query i iff i - w < j <= i)
@@ -37,7 +40,8 @@ FA_F16, FA_BF16 = 0, 1
 FA_MAX_SPLITS = 256
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
                 4: "FA_ERR_ALIGN", 5: "FA_ERR_UNSUPPORTED", 6: "FA_ERR_WORKSPACE",
-                7: "FA_ERR_HIP", 8: "FA_ERR_SPLITS"}
+                7: "FA_ERR_HIP", 8: "FA_ERR_SPLITS", 9: "FA_ERR_SCRATCH"}
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -77,6 +81,8 @@ def load_library(path: str = LIB_PATH):
     lib.fa_decode_ex.restype = i
     lib.fa_decode_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, i, vp]
     lib.fa_decode_varlen.restype = i
+    lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_decode_noalloc.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -249,6 +255,22 @@ def fa_decode_varlen(q, k, v, kv_lens, o, lse, scale: float, num_splits: int, wo
     _check(load_library().fa_decode_varlen(*args, B, H, hkv, Nkv, d, float(scale),
                                            int(num_splits), _dev(workspace, "workspace"), nbytes,
                                            _dt_code(k), _stream(k, stream)), "fa_decode_varlen")
+
+
+def fa_decode_noalloc(q, k, v, o, lse, scale: float, num_splits: int, stream=None):
+    """fa_decode_ex with the per-chunk partials in the library's static device scratch
+    (FA_NOALLOC_SCRATCH_BYTES) instead of a caller workspace: q [B,H,1,d], k/v
+    [B,H_kv,Nkv,d].  Calls that may run at the same time on one device race."""
+    torch = _torch()
+    B, H, _, d = q.shape
+    hkv = _kv_heads(q, k)
+    Nkv = k.shape[2]
+    args = [_dev(q, "q", k.dtype, (B, H, 1, d)), _dev(k, "k"), _dev(v, "v", k.dtype, k.shape),
+            _dev(o, "o", k.dtype, (B, H, 1, d)),
+            _dev(lse, "lse", torch.float32, (B, H)) if lse is not None else ctypes.c_void_p(0)]
+    _check(load_library().fa_decode_noalloc(*args, B, H, hkv, Nkv, d, float(scale),
+                                            int(num_splits), _dt_code(k), _stream(k, stream)),
+           "fa_decode_noalloc")
 
 
 # ------------------------------------------------------------------ convenience

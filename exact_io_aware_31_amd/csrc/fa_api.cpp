@@ -55,7 +55,8 @@ fa_status check_decode(const void* q, const void* k, const void* v, void* o, int
   return FA_OK;
 }
 
-// Shared body of fa_decode_ex and fa_decode_varlen (kv_lens may be null).
+// Shared body of fa_decode_ex and fa_decode_varlen (kv_lens may be null), and
+// of fa_decode_noalloc once its scratch is known.
 fa_status decode_impl(const void* q, const void* k, const void* v, const int* kv_lens, void* o,
                       float* lse, int B, int H, int H_kv, int Nkv, int d, float scale,
                       int num_splits, void* workspace, size_t workspace_bytes, fa_dtype dt,
@@ -153,6 +154,22 @@ fa_status fa_decode_ex(const void* q, const void* k, const void* v, void* o, flo
                      workspace_bytes, dt, stream);
 }
 
+fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int H_kv, int Nkv, int d, float scale, int num_splits,
+                            fa_dtype dt, void* stream) {
+  fa_status st = check_decode(q, k, v, o, B, H, H_kv, Nkv, d, scale, num_splits, dt);
+  if (st != FA_OK) return st;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return FA_ERR_ALIGN;
+  void* scratch = nullptr;
+  if (fa::noalloc_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+  return decode_impl(q, k, v, nullptr, o, lse, B, H, H_kv, Nkv, d, scale, num_splits, scratch,
+                     FA_NOALLOC_SCRATCH_BYTES, dt, stream);
+}
+
 fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                     int Nkv, int d, float scale, int num_splits, void* workspace,
                     size_t workspace_bytes, fa_dtype dt, void* stream) {
@@ -172,6 +189,9 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a kernel launch";
     case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits out of range";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the call needs more than the library's static decode scratch "
+             "(FA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown fa_status";
 }

@@ -19,8 +19,11 @@
 // the probabilities are rounded to the storage type, as the fused forward
 // pass rounds P for its P V product, and the output accumulates
 // v_dot2_f32 over pairs of keys: (v_a[i], v_b[i]) . (p_a, p_b).
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "../../include/fa.h"
 
 namespace fa {
 
@@ -351,6 +354,40 @@ static hipError_t launch_decode_dt(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   return a.dt == DType::BF16 ? launch_decode_dt<__bf16>(a, s) : launch_decode_dt<_Float16>(a, s);
+}
+
+// Scratch of fa_decode_noalloc, for callers that cannot allocate device
+// memory: the per-chunk partial outputs and log-sum-exps live in this
+// file-scope array, which every device the library runs on holds (its own
+// copy) until the process ends.  Host code never uses the array's name as an
+// address: the device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept.  Every chunk slot
+// the merge reads is written by the split kernel of the same call (empty
+// chunks included), so nothing needs clearing between calls; calls that
+// overlap on one device share the array and race.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` per device, once looked up
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -71,6 +71,11 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// Device address of fa_decode_noalloc's static scratch on the current device
+// (FA_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned), looked up on the first
+// call per device.
+hipError_t noalloc_scratch(void** ptr);
+
 // Workspace layouts (bytes), shared by the size queries and the launchers:
 // the backward's float32 row terms D [B, H, N]; the decode's float32 partial
 // outputs [B, H, splits, d], then partial log-sum-exps [B, H, splits]; each

@@ -40,8 +40,9 @@
  *     caller's next synchronisation.
  *   - Ownership: the caller allocates and owns every buffer, including the
  *     workspaces sized by the *_workspace_bytes queries.  The library never
- *     allocates or frees device memory and keeps no state between calls.
- *     Outputs must not alias inputs.
+ *     allocates or frees device memory; the one state it keeps is the device
+ *     address of fa_decode_noalloc's static scratch, looked up once per
+ *     device.  Outputs must not alias inputs.
  *   - Errors: every argument is validated before any HIP call; on a
  *     validation error (every code but FA_ERR_HIP) nothing is enqueued and
  *     no output is touched.  FA_ERR_HIP means the runtime refused a kernel
@@ -69,7 +70,8 @@ typedef enum fa_status {
   FA_ERR_UNSUPPORTED = 5, /* head dimension other than 64 or 128; window without causal */
   FA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the query says */
   FA_ERR_HIP = 7,         /* the HIP runtime refused a launch */
-  FA_ERR_SPLITS = 8       /* num_splits < 1 or above FA_MAX_SPLITS */
+  FA_ERR_SPLITS = 8,      /* num_splits < 1 or above FA_MAX_SPLITS */
+  FA_ERR_SCRATCH = 9      /* fa_decode_noalloc: the call needs more than FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 typedef enum fa_dtype { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
@@ -185,6 +187,34 @@ fa_status fa_decode_varlen(const void* q, const void* k, const void* v, const in
                            void* o, float* lse, int B, int H, int H_kv, int Nkv, int d,
                            float scale, int num_splits, void* workspace, size_t workspace_bytes,
                            fa_dtype dt, void* stream);
+
+/*
+ * Decode without any device allocation, for callers that cannot allocate:
+ * code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same computation and kernels as fa_decode_ex (same
+ * arguments, minus the workspace), with the per-chunk partial outputs and
+ * log-sum-exps held in a static device array of FA_NOALLOC_SCRATCH_BYTES
+ * inside the library instead of a caller workspace; the results are bitwise
+ * those of fa_decode_ex.
+ *   - The call needs fa_decode_workspace_bytes(B, H, d, num_splits) bytes of
+ *     it; more is FA_ERR_SCRATCH (checked before any HIP call).  For
+ *     example B = 64, H = 32, d = 128, 16 chunks need 16.1 MiB.
+ *   - Every GPU the library runs on holds its own copy of the array until the
+ *     process ends.  The first call on a device (with that device current)
+ *     looks up the array's address there with hipGetSymbolAddress; a failure
+ *     of that lookup is FA_ERR_HIP.
+ *   - Nothing in the array needs to start at zero: every chunk slot the merge
+ *     reads is written by the same call.
+ *   - All calls on one device share the array: calls whose kernels may run at
+ *     the same time on one device (other streams, other threads) race and
+ *     give undefined results.  Calls in order on one stream are safe.
+ *   - No allocation of any kind: no hipMalloc, hipFree or allocating library
+ *     routine is called.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int H_kv, int Nkv, int d, float scale, int num_splits,
+                            fa_dtype dt, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status s);

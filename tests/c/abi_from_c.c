@@ -31,7 +31,7 @@ int main(void) {
   fa_status s;
 
   printf("version %s\n", fa_version());
-  for (s = FA_OK; s <= FA_ERR_SPLITS; s = (fa_status)(s + 1))
+  for (s = FA_OK; s <= FA_ERR_SCRATCH; s = (fa_status)(s + 1))
     if (fa_status_string(s) == NULL || strlen(fa_status_string(s)) == 0) {
       printf("FAIL status string %d\n", (int)s);
       ++failures;
@@ -66,6 +66,12 @@ int main(void) {
   expect("decode_varlen null lengths",
          fa_decode_varlen(p, p, p, NULL, p, pf, 2, 4, 2, 50, 128, 0.1f, 4,
                           p, fa_decode_workspace_bytes(2, 4, 128, 4), FA_BF16, NULL),
+         FA_ERR_NULL);
+  expect("decode_noalloc beyond the static scratch",
+         fa_decode_noalloc(p, p, p, p, pf, 64, 64, 64, 50, 128, 0.1f, 32, FA_BF16, NULL),
+         FA_ERR_SCRATCH);
+  expect("decode_noalloc null q",
+         fa_decode_noalloc(NULL, p, p, p, pf, 2, 4, 2, 50, 128, 0.1f, 4, FA_BF16, NULL),
          FA_ERR_NULL);
   printf("%d failure(s)\n", failures);
   return failures != 0;

@@ -3,9 +3,10 @@
 //
 // The kernel launchers are replaced here by stand-ins that record the arguments the ABI layer
 // hands them and enqueue nothing, so the whole layer -- validation, workspace carving, the
-// window and grouped-head normalisation -- runs on a machine without a GPU.  Every call with
-// invalid arguments must fail with the documented status before reaching a launcher; every
-// valid call must reach exactly one launcher with the arguments the header describes.  Prints one line per check; exits non-zero on any failure.
+// window and grouped-head normalisation, the static-scratch path of fa_decode_noalloc -- runs
+// on a machine without a GPU.  Every call with invalid arguments must fail with the
+// documented status before reaching a launcher; every valid call must reach exactly one
+// launcher with the arguments the header describes.  Prints one line per check; exits non-zero on any failure.
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -19,6 +20,7 @@ fa::FwdArgs g_fwd;
 fa::BwdArgs g_bwd;
 fa::DecodeArgs g_dec;
 hipStream_t g_stream = nullptr;
+alignas(256) unsigned char g_fake_scratch[256];
 }  // namespace
 
 namespace fa {
@@ -38,6 +40,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   ++g_calls;
   g_dec = a;
   g_stream = s;
+  return hipSuccess;
+}
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = g_fake_scratch;
   return hipSuccess;
 }
 }  // namespace fa
@@ -150,6 +156,21 @@ int main() {
   expect("decode_varlen misaligned lengths",
          fa_decode_varlen(q, k, v, (const int*)odd, o, lse, 3, 8, 4, 1000, 64, 0.1f, 5, ws, dws,
                           FA_F16, nullptr), FA_ERR_ALIGN, n);
+
+  // decode without allocation: the same launch, on the library's static scratch
+  n = g_calls;
+  expect("decode_noalloc valid", fa_decode_noalloc(q, k, v, o, lse, 3, 8, 4, 1000, 64, 0.1f, 5,
+                                                   FA_F16, nullptr), FA_OK, n);
+  check("decode_noalloc carves the static scratch like a workspace",
+        g_dec.part_o == (float*)g_fake_scratch &&
+            g_dec.part_lse == (float*)(g_fake_scratch + po) && g_dec.splits == 5);
+  n = g_calls;
+  expect("decode_noalloc beyond the scratch",
+         fa_decode_noalloc(q, k, v, o, lse, 64, 64, 64, 1000, 128, 0.1f, 32, FA_BF16, nullptr),
+         FA_ERR_SCRATCH, n);
+  expect("decode_noalloc misaligned o",
+         fa_decode_noalloc(q, k, v, odd, lse, 3, 8, 4, 1000, 64, 0.1f, 5, FA_F16, nullptr),
+         FA_ERR_ALIGN, n);
 
   for (int s = -1; s <= 10; ++s) check("status string", fa_status_string((fa_status)s) != nullptr &&
                                                             strlen(fa_status_string((fa_status)s)) > 0);

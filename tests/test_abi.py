@@ -36,7 +36,7 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_decode", "fa_fwd_ex", "fa_bwd_ex",
-                          "fa_decode_ex", "fa_decode_varlen",
+                          "fa_decode_ex", "fa_decode_varlen", "fa_decode_noalloc",
                           "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_version"}
     for n in names:
@@ -172,6 +172,28 @@ def test_decode_varlen_validation(lib):
     assert call(H_kv=3) == ERR["FA_ERR_SHAPE"]
     assert call(splits=0) == ERR["FA_ERR_SPLITS"]
     assert call(d=32) == ERR["FA_ERR_UNSUPPORTED"]
+
+
+def test_decode_noalloc_validation(lib):
+    """Checks run before any HIP call: a call needing more than the static scratch is refused
+    with FA_ERR_SCRATCH; the other checks are fa_decode_ex's."""
+    def call(q=P, k=P, v=P, o=P, lse=P, B=2, H=8, H_kv=2, Nkv=100, d=128, splits=4, dt=1):
+        return lib.fa_decode_noalloc(q, k, v, o, lse, B, H, H_kv, Nkv, d, 0.1, splits, dt, NULL)
+    for kw in ("q", "k", "v", "o"):
+        assert call(**{kw: NULL}) == ERR["FA_ERR_NULL"]
+    assert call(H_kv=3) == ERR["FA_ERR_SHAPE"]
+    assert call(splits=0) == ERR["FA_ERR_SPLITS"]
+    assert call(d=80) == ERR["FA_ERR_UNSUPPORTED"]
+    assert call(dt=5) == ERR["FA_ERR_DTYPE"]
+    assert call(o=P_ODD) == ERR["FA_ERR_ALIGN"]
+    # 64 x 64 heads x 32 chunks x (128 + 1) floats = 64.5 MiB > 32 MiB
+    assert fa.fa_decode_workspace_bytes(64, 64, 128, 32) > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert call(B=64, H=64, H_kv=64, splits=32) == ERR["FA_ERR_SCRATCH"]
+    # the decode of the B64 H32 d128 16-chunk workload fits
+    assert fa.fa_decode_workspace_bytes(64, 32, 128, 16) <= fa.FA_NOALLOC_SCRATCH_BYTES
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_NOALLOC_SCRATCH_BYTES
 
 
 def test_probe_library_exports_every_declared_function():
