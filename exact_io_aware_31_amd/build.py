@@ -10,9 +10,16 @@ canonicalisations.
 Output: exact_io_aware_31_amd/_lib/libfa.so (the attention library) and
 exact_io_aware_31_amd/_lib/libfa_probe.so (the two measurement kernels of
 include/fa_probe.h, used by the benchmark to measure the chip's own ceilings).
+
+Every HIP source is compiled with the backend's kernel resource report; the
+per-kernel registers, occupancy and scratch are written to
+_build/kernel_resources.txt, and the build fails if any kernel spills to
+scratch memory (a spill turns register traffic into memory traffic on every
+loop iteration).
 """
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -42,21 +49,57 @@ def common_flags():
             "-fno-honor-nans"]
 
 
+def _resources(text: str):
+    """(kernel, VGPRs, AGPRs, scratch bytes per lane, waves per SIMD) from the backend's
+    kernel-resource-usage remarks."""
+    out, cur = [], None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = {"name": m.group(1)}
+            out.append(cur)
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).split()[0]] = int(m.group(2))
+    return out
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    lang = ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
     cmd = [hipcc()] + common_flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature; that is expected.
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and ln.strip()]
+    text = r.stdout + r.stderr
+    msgs = [ln for ln in text.splitlines()
+            if noise not in ln and "kernel-resource-usage" not in ln and ln.strip()]
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
+    if src.endswith(".hip"):
+        with open(obj + ".resources", "w") as f:
+            for k in _resources(text):
+                f.write(f"{k['name']} vgpr={k.get('VGPRs', -1)} agpr={k.get('AGPRs', -1)} "
+                        f"scratch={k.get('ScratchSize', -1)} waves_per_simd={k.get('Occupancy', -1)}\n")
     return obj
+
+
+def _check_resources(objs) -> None:
+    """Write _build/kernel_resources.txt; fail if a kernel uses scratch memory."""
+    lines = []
+    for o in objs:
+        if os.path.exists(o + ".resources"):
+            lines += open(o + ".resources").read().splitlines()
+    with open(os.path.join(BUILD_DIR, "kernel_resources.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    spills = [ln for ln in lines if "scratch=0 " not in ln]
+    if spills:
+        raise RuntimeError("kernels using scratch memory (register spills):\n" + "\n".join(spills))
 
 
 def _link(objs, lib: str, verbose: bool) -> None:
@@ -75,6 +118,7 @@ def build_library(verbose: bool = False) -> str:
     os.makedirs(LIB_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
+    _check_resources(objs)
     _link(objs[:len(SOURCES)], LIB, verbose)
     _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB

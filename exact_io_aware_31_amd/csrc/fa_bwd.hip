@@ -70,6 +70,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 constexpr int KV_WAVES = 4;
 constexpr int KV_BK = 32 * KV_WAVES;  // keys per workgroup
 constexpr int KV_BQ = 32;             // query rows per step
+constexpr int KV_READ_AHEAD = 3;      // S / dP MFMAs whose LDS operands are read ahead
 
 template <typename T, int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
@@ -157,9 +158,12 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     step_loader.load(Q + qoff, N, qi0, Qs[buf], wave);
     step_loader.load(dO + qoff, N, qi0, dOs[buf], wave);
     if (tid < BQ) {
-      const int qrow = qi0 + tid;
-      lpre = (qrow < N) ? LSE[(size_t)qh * N + qrow] * 1.4426950408889634f : 0.f;
-      dpre = (qrow < N) ? drow[(size_t)qh * N + qrow] : 0.f;
+      // Rows qi0 + tid of the head's L and D through a buffer descriptor of
+      // the rows from qi0 on: rows past the end read as zero (their
+      // probabilities are masked), and no lane holds a 64-bit address.
+      const uint32_t bytes = (uint32_t)(N - qi0) * 4u;
+      lpre = buffer_load_f32(LSE + (size_t)qh * N + qi0, bytes, 4u * tid) * 1.4426950408889634f;
+      dpre = buffer_load_f32(drow + (size_t)qh * N + qi0, bytes, 4u * tid);
     }
   };
   auto store_step = [&](int buf) {
@@ -190,8 +194,6 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     // being hoisted into sixteen loop-invariant registers.
     uint32_t rbs = rb + buf * (BQ * D * 2), tbs = tb + buf * (BQ * D * 2), kws = kwb;
     asm volatile("" : "+v"(rbs), "+v"(tbs), "+v"(kws));
-    // Let the scheduler interleave the LDS reads with the matrix products.
-    __builtin_amdgcn_iglp_opt(0);
     // Visibility: query qi0 + ql sees key mykey iff ql >= mykey - qi0 (causal),
     // the query exists (ql < N - qi0) and the key exists.
     // Window: query qi0 + ql also needs ql < mykey + window - qi0.
@@ -219,6 +221,25 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     for (int kk = 0; kk < D / 16; ++kk) {
       const v8 ad = lds_at<v8>(dOs[0], rbs ^ (32 * kk));
       dp = mfma32x32x16(ad, vf[kk], dp);
+    }
+    // Issue order of the two products: each MFMA's LDS operands are read
+    // KV_READ_AHEAD MFMAs ahead of it (two reads per S MFMA, one per dP MFMA),
+    // instead of the scheduler's read-wait-use pairs, which expose the LDS
+    // latency at every MFMA of the S chain.
+    {
+      constexpr int NS = D / 16, L = NS < KV_READ_AHEAD ? NS : KV_READ_AHEAD;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * L, 0);
+#pragma unroll
+      for (int i = 0; i < NS - L; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, L, 0);
     }
     // P = exp2(c S - L log2 e) for every element, then, on the few steps that
     // need it (the wave's diagonal step and the ragged ends), the masked
@@ -254,12 +275,19 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
         const u32x4 cd = {d0[0], d0[1], d1[0], d1[1]};
         dvacc[nb] = mfma32x32x16(pA[kc], __builtin_bit_cast(v8, cd), dvacc[nb]);
       }
-    // dS = P o (dP - D) with P as rounded for the P^T dO product (dS is
-    // rounded to the storage type as well).
+    // dS = P o (dP - D), rounded to the storage type.  For bfloat16, P as
+    // rounded for the P^T dO product (unpacked from the packed words); for
+    // fp16, the fp32 P, as in the dQ pass (the fp16 unpacking costs the
+    // registers that keep this kernel out of scratch memory).
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       float pr[8], dsv[8];
-      from_v8(pA[hf], pr);
+      if constexpr (__is_same(T, __bf16)) {
+        from_v8(pA[hf], pr);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = pv[8 * hf + e];
+      }
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][16 * hf + 8 * g2 + 4 * hh]);
@@ -303,6 +331,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
 // a three-deep ring) by default, four (two workgroups per CU, a two-deep
 // ring) when the grid of 256-row blocks is small, as in the forward pass.
 constexpr int DQ_BC = 64;  // keys per tile
+constexpr int DQ_READ_AHEAD = 6;  // S / dP MFMAs whose LDS operands are read ahead
 constexpr long DQ_SMALL_GRID = 256;  // 256-row blocks below which dQ runs four-wave workgroups
 
 template <typename T, int D, bool CAUSAL, bool WIN, int NW>
@@ -424,6 +453,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
             s[sb] = mfma32x32x16(ak, qf[kk], s[sb]);
             dp[sb] = mfma32x32x16(av, dof[kk], dp[sb]);
           }
+        }
+        // Issue order: each K or V row read runs DQ_READ_AHEAD MFMAs ahead of
+        // the MFMA that uses it (the scheduler's read-wait-use pairs expose
+        // the LDS latency at every one of these MFMAs).
+        {
+          constexpr int NM = 2 * (BC / 32) * (D / 16), L = DQ_READ_AHEAD;
+          __builtin_amdgcn_sched_group_barrier(0x100, L, 0);
+#pragma unroll
+          for (int i = 0; i < NM - L; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, L, 0);
         }
         if (need_mask) {
 #pragma unroll

@@ -13,6 +13,18 @@ using fa::bf16x8;
 using fa::f32x16;
 using fa::u32x4;
 
+// A pseudo-random value in [-1, 1) with a full mantissa: the matrix cores'
+// power draw, and so the clock they sustain, depends on how many operand bits
+// switch, so the probe's operands look like attention data (N(0,1)-like bf16
+// values), not like small round numbers.
+__device__ __forceinline__ float probe_value(uint32_t x) {
+  x = x * 2654435761u + 0x9e3779b9u;
+  x ^= x >> 15;
+  x *= 2246822519u;
+  x ^= x >> 13;
+  return (float)(x >> 8) * (1.0f / 8388608.0f) - 1.0f;
+}
+
 // Four independent accumulate chains per wave, operands in registers.  The
 // empty asm statements order the clock reads around the loop: the first
 // makes the loop's operand depend on an instruction issued after the first
@@ -24,8 +36,8 @@ __global__ __launch_bounds__(FA_PROBE_THREADS) void mfma_probe_kernel(float* __r
   bf16x8 a, b;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)((float)((lane + i) % 7 + 1) * (1.0f / 256.0f));
-    b[i] = (__bf16)((float)((lane * 3 + i) % 5 + 1) * (1.0f / 256.0f));
+    a[i] = (__bf16)probe_value((uint32_t)(blockIdx.x * 4096 + tid * 16 + i));
+    b[i] = (__bf16)probe_value((uint32_t)(blockIdx.x * 4096 + tid * 16 + 8 + i) ^ 0x5bd1e995u);
   }
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
@@ -54,7 +66,9 @@ __global__ __launch_bounds__(FA_PROBE_THREADS) void mfma_probe_kernel(float* __r
 
 // Chunk c covers 16-byte elements c * 4096 .. c * 4096 + 4095; lane t of a
 // workgroup loads elements t + 256 u, u = 0..15, so every load instruction of
-// a wave reads 1 KiB of consecutive bytes.  Workgroups stride over chunks.
+// a wave reads 1 KiB of consecutive bytes.  Workgroup b reads the contiguous
+// run of chunks b * cpb .. b * cpb + cpb - 1 (cpb = ceil(chunks / workgroups)),
+// as a decode workgroup streams its own part of a history.
 constexpr int kLoads = FA_PROBE_READ_CHUNK / (16 * FA_PROBE_THREADS);
 static_assert(kLoads == 16, "sixteen 16-byte loads per lane per chunk");
 
@@ -62,8 +76,11 @@ __global__ __launch_bounds__(FA_PROBE_THREADS) void stream_read_kernel(const u32
                                                                        size_t nchunks,
                                                                        unsigned* __restrict__ out) {
   const int tid = threadIdx.x;
+  const size_t cpb = (nchunks + gridDim.x - 1) / gridDim.x;
+  const size_t c0 = (size_t)blockIdx.x * cpb;
+  const size_t c1 = c0 + cpb < nchunks ? c0 + cpb : nchunks;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (size_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+  for (size_t c = c0; c < c1; ++c) {
     const u32x4* __restrict__ p = buf + c * (size_t)(kLoads * FA_PROBE_THREADS) + tid;
     u32x4 v[kLoads];
 #pragma unroll

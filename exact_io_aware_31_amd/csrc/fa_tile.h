@@ -77,6 +77,14 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t byt
                                            voff, 0, 0, 0);
 }
 
+// One float through a raw buffer descriptor of `bytes` bytes at base (both
+// wave-uniform): offsets voff at or past `bytes` read as zero.
+__device__ __forceinline__ float buffer_load_f32(const float* base, uint32_t bytes, uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+}
+
 // Direct load of rows kb .. kb + BC - 1 of a head into the tile at dst by NW
 // waves (buffer_load_dwordx4 ... lds): the tile is cut into 1 KiB segments,
 // wave w fills segments w SPW .. w SPW + SPW - 1, and lane l of segment g

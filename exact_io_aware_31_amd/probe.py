@@ -85,12 +85,13 @@ def mfma_bf16_rate(torch, iters: int = 40000, reps: int = 3, waves_per_simd=(1, 
             best = rec
         del out, stamps
     best["what"] = ("dense bf16 v_mfma_f32_32x32x16 rate, four register-operand chains per wave, "
+                    "pseudo-random full-mantissa operands in [-1, 1), "
                     f"best of {list(waves_per_simd)} waves per SIMD on {cus} CUs")
     return best
 
 
 def stream_read_rate(torch, nbytes: int = 8 << 30, reps: int = 5,
-                     blocks=(1024, 2048, 4096, 8192, 32768)):
+                     blocks=(2048, 4096, 8192, 16384, 32768, 65536)):
     """Best streaming-read rate (16-byte non-temporal loads) over a few grid sizes; median of
     reps per grid size."""
     lib = load_library()
@@ -114,5 +115,6 @@ def stream_read_rate(torch, nbytes: int = 8 << 30, reps: int = 5,
     del buf
     torch.cuda.empty_cache()
     best["what"] = (f"streaming read of {nbytes >> 20} MiB, 16-byte non-temporal loads, sixteen in "
-                    f"flight per lane, best of grids {list(blocks)} (median of {reps})")
+                    f"flight per lane, a contiguous run per workgroup, best of grids {list(blocks)} "
+                    f"(median of {reps})")
     return best

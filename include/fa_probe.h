@@ -33,7 +33,10 @@ extern "C" {
  * Dense bf16 matrix-core rate.  `blocks` workgroups of four waves; every
  * wave runs `iters` rounds of four independent v_mfma_f32_32x32x16_bf16
  * accumulate chains on register operands (no memory traffic inside the
- * loop), i.e. blocks * 4 * iters * 4 * 32768 FLOP in total.
+ * loop), i.e. blocks * 4 * iters * 4 * 32768 FLOP in total.  The operands are
+ * pseudo-random bf16 values in [-1, 1) with full mantissas: the clock the
+ * matrix cores sustain depends on the data, and attention operands are of
+ * this kind.
  *   out    : device float32 [blocks * FA_PROBE_THREADS], 4-byte aligned: one
  *            sum of each lane's accumulators (keeps the products live).
  *   stamps : device uint64 [4], 8-byte aligned: workgroup 0, wave 0 writes the
@@ -50,7 +53,7 @@ int fa_probe_mfma_bf16(float* out, unsigned long long* stamps, int blocks, int i
 /*
  * Streaming HBM read rate.  `blocks` workgroups read every byte of buf once
  * with 16-byte non-temporal loads (sixteen in flight per lane) and XOR-reduce
- * them.
+ * them; each workgroup reads one contiguous run of chunks.
  *   buf   : device, 16-byte aligned, `bytes` bytes, bytes a non-zero multiple
  *           of FA_PROBE_READ_CHUNK.  Its contents do not matter.
  *   out   : device uint32 [blocks * FA_PROBE_THREADS], 4-byte aligned.
