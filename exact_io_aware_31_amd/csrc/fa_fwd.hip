@@ -366,14 +366,16 @@ static hipError_t launch_fwd_nw(const FwdArgs& a, hipStream_t s) {
 }
 
 // Fewer than four 256-row blocks per CU (1024 on the 256 CUs): four-wave
-// workgroups, two per CU, keep the SIMDs fed (measured: B4 H16 N2048
-// causal runs 13% faster so; at B1 H32 N8192, 1024 blocks, the eight-wave
-// shape is 4.5% faster, as its K/V tiles serve twice the rows).
+// workgroups, two per CU, keep the SIMDs fed.  Measured, interleaved on one
+// box (outputs bitwise identical): B4 H16 N2048 causal 0.0795 ms against
+// 0.0805 with eight-wave workgroups; at B1 H32 N8192, 1024 blocks, the
+// eight-wave shape is faster, 0.4950 against 0.5004 ms, as its K/V tiles
+// serve twice the rows.
 constexpr long FWD_SMALL_GRID = 1024;
 
 // A sliding window of up to 2048 keys bounds each block's work to a few
 // tiles, so the smaller blocks win there too (window 1024 at B1 H32 N8192:
-// 0.169 -> 0.158 ms).
+// 0.1665 ms with eight-wave workgroups, 0.1483 with four-wave ones).
 constexpr int FWD_SMALL_WINDOW = 2048;
 
 template <typename T, int D, bool CAUSAL, bool WIN>
