@@ -156,10 +156,15 @@ def roofline(workload, entry, bound, amount, ms_list, index, peaks):
     r["profiled_ms"] = round(float(prof["kernel_us"]) / 1e3, 4) if prof else None
     clock = float(prof["clock_ghz"]) if prof and prof.get("clock_ghz") not in (None, "na") else None
     r["clock_ghz"] = clock
-    if bound == "mfma" and clock:
-        pc = PEAK_BF16_TFLOPS * clock / SPEC_CLOCK_GHZ
+    # The published peak scaled to a clock under matrix load: the probe's, measured on this machine
+    # in this run, else the profiled kernel's (another run, possibly another box).
+    probe_clock = (peaks or {}).get("mfma", {}).get("clock_ghz")
+    scale_clock, source = (probe_clock, "probe, this run") if probe_clock else (clock, "profile")
+    if bound == "mfma" and scale_clock:
+        pc = PEAK_BF16_TFLOPS * scale_clock / SPEC_CLOCK_GHZ
         r["peak_at_clock"] = round(pc, 1)
         r["frac_at_clock"] = round(achieved / pc, 4)
+        r["clock_for_peak"] = {"ghz": scale_clock, "source": source}
     if prof and prof.get("mfma_busy") not in (None, "na"):
         r["mfma_busy"] = float(prof["mfma_busy"])
     return r

@@ -105,8 +105,15 @@ def test_roofline_arithmetic():
     assert r["achieved_at_median"] == 500.0 and r["achieved_at_min"] == 1000.0
     assert r["peak_measured"] == 2000.0 and r["frac_measured"] == 0.25
     assert r["traffic"] == 1000.0 and r["traffic_ratio"] == 2.0 and r["profiled_ms"] == 1.5
+    # without a probe clock the published peak is scaled to the profiled clock ...
     assert r["clock_ghz"] == 1.8 and r["peak_at_clock"] == 1875.0
     assert r["frac_at_clock"] == round(500.0 / 1875.0, 4) and r["mfma_busy"] == 0.5
+    assert r["clock_for_peak"] == {"ghz": 1.8, "source": "profile"}
+    # ... and with one, to the clock the probe measured in the same run
+    peaks_clk = {"mfma": {"tflops": 2000.0, "clock_ghz": 1.92}, "read": {"gbs": 7000.0}}
+    r = bench.roofline("w", "fa_fwd", "mfma", 1e12, [2.0], idx, peaks_clk)
+    assert r["peak_at_clock"] == 2000.0 and r["frac_at_clock"] == 0.25
+    assert r["clock_for_peak"] == {"ghz": 1.92, "source": "probe, this run"} and r["clock_ghz"] == 1.8
     # an HBM-bound entry against the measured read ceiling; no profile figures without an index
     r = bench.roofline("d", "fa_decode", "hbm", 8e9, [2.0], {}, peaks)
     assert r["achieved"] == 4000.0 and r["frac"] == 0.5 and r["frac_measured"] == round(4 / 7, 4)
