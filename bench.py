@@ -62,7 +62,7 @@ INDEX_FILE = os.path.join(ROOT, "profiles", "roofline_index.txt")
 # Each kernel family's source and the device headers it includes.
 KERNEL_SOURCES = {"fwd": ("fa_fwd.hip", "fa_tile.h", "fa_common.h"),
                   "bwd": ("fa_bwd.hip", "fa_tile.h", "fa_common.h"),
-                  "decode": ("fa_decode.hip", "fa_common.h")}
+                  "decode": ("fa_decode.hip", "fa_tile.h", "fa_common.h")}
 FAMILY = {"fa_fwd": "fwd", "fa_fwd_ex": "fwd", "fa_bwd": "bwd", "fa_decode": "decode",
           "fa_decode_ex": "decode", "fa_decode_varlen": "decode"}
 BWD_8K_NAME = "bwd_b1h32n8192d128_bf16_causal_q2"

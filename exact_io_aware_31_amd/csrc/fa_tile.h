@@ -69,12 +69,15 @@ __device__ __forceinline__ u32x2 lds_tr_at(const void* tile, uint32_t byte_off) 
 // byte offset voff of a raw buffer of `bytes` bytes starting at base, land at
 // lds_base + 16 l (lds_base wave-uniform).  Offsets at or past `bytes` read
 // as zero.  base and bytes must be wave-uniform (they form the descriptor).
+// CPOL is the load's cache policy (0, or FA_CPOL_NT for data read once).
+#define FA_CPOL_NT 2
+template <int CPOL = 0>
 __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t bytes, uint32_t voff,
                                                   void* lds_base) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           voff, 0, 0, 0);
+                                           voff, 0, 0, CPOL);
 }
 
 // One float through a raw buffer descriptor of `bytes` bytes at base (both
@@ -111,13 +114,15 @@ struct TileLoader {
       voff[i] = 2u * (uint32_t)(row * D + 8 * ((lane % (D / 8)) ^ SW::sw(row)));
     }
   }
-  // Rows kb .. kb + BC - 1 of a head of N rows (kb < N) into the tile at dst.
-  template <typename T>
+  // Rows kb .. kb + BC - 1 of a head of N rows (kb <= N; with kb = N nothing
+  // is read and the loads land zeros) into the tile at dst.
+  template <int CPOL = 0, typename T>
   __device__ __forceinline__ void load(const T* head, int N, int kb, T* dst, int wave) const {
     const uint32_t bytes = (uint32_t)(N - kb) * (uint32_t)(D * 2);
     const void* base = head + (size_t)kb * D;
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) buffer_load_lds16(base, bytes, voff[i], dst + (wave * SPW + i) * 512);
+    for (int i = 0; i < SPW; ++i)
+      buffer_load_lds16<CPOL>(base, bytes, voff[i], dst + (wave * SPW + i) * 512);
   }
 };
 
