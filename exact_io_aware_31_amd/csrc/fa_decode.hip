@@ -63,18 +63,16 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-// Sum over the WIDTH consecutive lanes (8 or 16, aligned) that share a key
+// Sum over the WIDTH consecutive lanes (4 or 8, aligned) that share a key
 // row, with DPP lane moves instead of LDS permutes: swap neighbours and
-// pairs inside each quad (quad_perm 1,0,3,2 and 2,3,0,1), then mirror within
-// each 8-lane half-row (every lane now holds its 8-lane sum) and, for 16,
-// within the 16-lane row.
+// pairs inside each quad (quad_perm 1,0,3,2 and 2,3,0,1), then, for 8,
+// mirror within each 8-lane half-row (every lane now holds its 8-lane sum).
 template <int WIDTH>
 __device__ __forceinline__ float row_sum(float x) {
-  static_assert(WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "4-, 8- or 16-lane rows");
+  static_assert(WIDTH == 4 || WIDTH == 8, "4- or 8-lane rows");
   x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
   x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
-  if (WIDTH >= 8) x = dpp_add<0x141>(x);  // row_half_mirror
-  if (WIDTH == 16) x = dpp_add<0x140>(x);  // row_mirror
+  if (WIDTH == 8) x = dpp_add<0x141>(x);  // row_half_mirror
   return x;
 }
 
