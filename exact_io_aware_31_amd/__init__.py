@@ -322,15 +322,20 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
     return dq, dk, dv
 
 
-def attention_decode(q, k, v, scale=None, num_splits=16, workspace=None, stream=None):
+def attention_decode(q, k, v, scale=None, num_splits=16, workspace=None, stream=None,
+                     kv_lens=None):
     """Allocate o, lse (and workspace if not given) and run fa_decode (fa_decode_ex when k, v
-    have fewer heads than q).  Returns (o, lse)."""
+    have fewer heads than q; fa_decode_varlen when kv_lens, a device int32 [B] of history
+    lengths, is given).  Returns (o, lse)."""
     torch = _torch()
     B, H, _, d = q.shape
     o = torch.empty((B, H, 1, d), dtype=k.dtype, device=k.device)
     lse = torch.empty((B, H), dtype=torch.float32, device=k.device)
     ws = decode_workspace(k, num_splits, heads=H) if workspace is None else workspace
-    if k.shape[1] != H:
+    if kv_lens is not None:
+        fa_decode_varlen(q, k, v, kv_lens, o, lse, _default_scale(d, scale), num_splits, ws,
+                         stream)
+    elif k.shape[1] != H:
         fa_decode_ex(q, k, v, o, lse, _default_scale(d, scale), num_splits, ws, stream)
     else:
         fa_decode(q, k, v, o, lse, _default_scale(d, scale), num_splits, ws, stream)

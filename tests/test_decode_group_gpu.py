@@ -186,3 +186,16 @@ def test_decode_group_full_size_workload(ragged):
         check_max_abs(np.array(lse_h[b, h]), np.array(lse_ref), w.dtype, f"lse head ({b},{h})")
     del k, v
     torch.cuda.empty_cache()
+
+
+def test_attention_decode_with_history_lengths():
+    """The binding's attention_decode(kv_lens=...) is fa_decode_varlen: bitwise the same output."""
+    B, H, Hkv, Nkv, d, dtype, splits = 3, 8, 2, 500, 128, torch.bfloat16, 4
+    announce(f"attention_decode kv_lens B{B} H{H} Hkv{Hkv} Nkv{Nkv} splits={splits}")
+    q, k, v = (t.to(DEV) for t in attention_inputs(B, H, 1, d, dtype, 9695, "cpu", Nkv=Nkv,
+                                                    Hkv=Hkv))
+    kv_lens = torch.tensor([500, 0, 77], dtype=torch.int32, device=DEV)
+    o1, l1 = fa.attention_decode(q, k, v, d ** -0.5, num_splits=splits, kv_lens=kv_lens)
+    o2, l2 = run_decode(q, k, v, d ** -0.5, splits, kv_lens)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
