@@ -313,17 +313,31 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     __syncthreads();
   }
 
-  // Write dK = scale * sum dS^T Q and dV = sum P^T dO for this wave's keys.
+  // Write dK = scale * sum dS^T Q and dV = sum P^T dO for this wave's keys,
+  // through LDS: in the accumulator layout a lane holds one column of 16 keys,
+  // so direct stores would be 2-byte pieces; staged row-major in the wave's
+  // own 32 rows of the K tile (free after the last step's barrier), every
+  // store instruction writes whole rows, 1 KiB contiguous.  dK first, then dV
+  // through the same rows.
+  T* const stage = Ks + 32 * D * wave;
+  constexpr int LPR = D / 8;    // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;  // rows per store instruction
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (key < N) {
-        dK[hoff + (size_t)key * D + 32 * nb + l32] = (T)(dkacc[nb][r] * scale);
-        dV[hoff + (size_t)key * D + 32 * nb + l32] = (T)dvacc[nb][r];
-      }
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        stage[tile_off<D>(8 * (r >> 2) + 4 * hh + (r & 3), 32 * nb + l32)] =
+            t2 == 0 ? (T)(dkacc[nb][r] * scale) : (T)dvacc[nb][r];
+    T* __restrict__ dst = t2 == 0 ? dK : dV;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = RPI * i + lane / LPR, ch = lane % LPR;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(stage + tile_off<D>(row, 8 * ch));
+      if (kw0 + row < N) st16(dst + hoff + (size_t)(kw0 + row) * D + 8 * ch, w);
     }
+  }
 }
 
 // ---------------------------------------------------------------- kernel 3
@@ -523,18 +537,29 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
     }
   }
 
-  // dQ = scale * dQ^T transposed back: lane writes row myq.
-  if (q_ok) {
-    T* __restrict__ qrow = dQ + hoff + (size_t)myq * D;
+  // dQ = scale * dQ^T, transposed back through LDS as in the forward pass: in
+  // the accumulator layout a lane holds 8-byte pieces of one row, so a store
+  // instruction would touch 32 rows; staged in a swizzled row-major tile (the
+  // ring is free after the last tile's barrier, half a ring buffer per wave),
+  // every store instruction writes whole rows, 1 KiB contiguous.
+  T* const stage = (wave < 2 ? K0 : wave < 4 ? K1 : wave < 6 ? K2 : V0) + (wave & 1) * 32 * D;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        v4 vals;
+    for (int gg = 0; gg < 4; ++gg) {
+      v4 vals;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) vals[q] = (T)(dqacc[nb][4 * gg + q] * scale);
-        *reinterpret_cast<u32x2*>(qrow + 32 * nb + 8 * gg + 4 * hh) = __builtin_bit_cast(u32x2, vals);
-      }
+      for (int q = 0; q < 4; ++q) vals[q] = (T)(dqacc[nb][4 * gg + q] * scale);
+      *reinterpret_cast<u32x2*>(stage + tile_off<D>(l32, 32 * nb + 8 * gg + 4 * hh)) =
+          __builtin_bit_cast(u32x2, vals);
+    }
+  constexpr int LPR = D / 8;    // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;  // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + lane / LPR, ch = lane % LPR;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(stage + tile_off<D>(row, 8 * ch));
+    if (qw0 + row < N) st16(dQ + hoff + (size_t)(qw0 + row) * D + 8 * ch, w);
   }
 }
 

@@ -332,24 +332,35 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     }
   }
 
-  // Epilogue: O = O / l, lse = (m + log2 l) ln 2.
+  // Epilogue: O = O / l, lse = (m + log2 l) ln 2.  The output goes through
+  // LDS: in the accumulator layout a lane holds 8-byte pieces of one row, so
+  // a store instruction would touch 32 rows with 16 bytes each; staged in a
+  // swizzled row-major tile, every store instruction writes whole rows, 1 KiB
+  // contiguous.  The K/V ring is free after the last tile's barrier; each
+  // wave stages its own 32 rows in half of one ring buffer.
+  static_assert(QG == 1, "one 32-row group per wave");
+  T* const stage = (wave < 2 ? K0 : wave < 4 ? K1 : wave < 6 ? K2 : V0) + (wave & 1) * 32 * D;
+  const float l_tot = half_pair_sum(l_run[0]);
+  const float inv = 1.f / l_tot;
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const float l_tot = half_pair_sum(l_run[g]);
-    const float inv = 1.f / l_tot;
-    if (myq[g] < N) {
-      T* __restrict__ orow = O + hoff + (size_t)myq[g] * D;
+  for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb)
+    for (int gg = 0; gg < 4; ++gg) {
+      v4 vals;
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          v4 vals;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) vals[q] = (T)(oacc[g][nb][4 * gg + q] * inv);
-          *reinterpret_cast<u32x2*>(orow + 32 * nb + 8 * gg + 4 * hh) = __builtin_bit_cast(u32x2, vals);
-        }
-      if (hh == 0) LSE[(size_t)bh * N + myq[g]] = (m_run[g] + log2f(l_tot)) * 0.69314718055994531f;
+      for (int q = 0; q < 4; ++q) vals[q] = (T)(oacc[0][nb][4 * gg + q] * inv);
+      *reinterpret_cast<u32x2*>(stage + tile_off<D>(l32, 32 * nb + 8 * gg + 4 * hh)) =
+          __builtin_bit_cast(u32x2, vals);
     }
+  if (myq[0] < N && hh == 0)
+    LSE[(size_t)bh * N + myq[0]] = (m_run[0] + log2f(l_tot)) * 0.69314718055994531f;
+  constexpr int LPR = D / 8;    // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;  // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + lane / LPR, ch = lane % LPR;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(stage + tile_off<D>(row, 8 * ch));
+    if (qw0 + row < N) st16(O + hoff + (size_t)(qw0 + row) * D + 8 * ch, w);
   }
 }
 
