@@ -66,6 +66,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
   if (row < rows && col == 0) drow[row] = s;
 }
 
+// p, an address in LDS, with its provenance hidden from the compiler: it
+// cannot tell which shared array the result points into.
+template <typename T>
+__device__ __forceinline__ T* opaque_lds(T* p) {
+  uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T*)p;
+  asm volatile("" : "+s"(a));
+  return (T*)(__attribute__((address_space(3))) T*)(uintptr_t)a;
+}
+
 // ---------------------------------------------------------------- kernel 2
 constexpr int KV_WAVES = 4;
 constexpr int KV_BK = 32 * KV_WAVES;  // keys per workgroup
@@ -151,25 +160,31 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
       ++qh;
     }
   };
-  float lpre = 0.f, dpre = 0.f;
+  float lraw = 0.f, draw = 0.f;
   const TileLoader<D, BQ, KV_WAVES> step_loader(wave, lane);
   auto load_step = [&](int qh, int qi0, int buf) {
     const size_t qoff = (size_t)qh * N * D;
-    step_loader.load(Q + qoff, N, qi0, Qs[buf], wave);
-    step_loader.load(dO + qoff, N, qi0, dOs[buf], wave);
-    if (tid < BQ) {
-      // Rows qi0 + tid of the head's L and D through a buffer descriptor of
-      // the rows from qi0 on: rows past the end read as zero (their
-      // probabilities are masked), and no lane holds a 64-bit address.
-      const uint32_t bytes = (uint32_t)(N - qi0) * 4u;
-      lpre = buffer_load_f32(LSE + (size_t)qh * N + qi0, bytes, 4u * tid) * 1.4426950408889634f;
-      dpre = buffer_load_f32(drow + (size_t)qh * N + qi0, bytes, 4u * tid);
-    }
+    // The direct loads name their ring slot through an opaque LDS address.
+    // Loads into a slot the compiler can trace (the Qs / dOs arrays) make it
+    // wait for them before every later read of the same array, including
+    // the reads of the other slot, which is this step's: the next step's
+    // tiles would have to arrive before this step could start.  The slots
+    // are ordered by the wait and the barrier that end every step instead.
+    step_loader.load(Q + qoff, N, qi0, opaque_lds(Qs[buf]), wave);
+    step_loader.load(dO + qoff, N, qi0, opaque_lds(dOs[buf]), wave);
+    // Rows qi0 + l32 of the head's L and D through a buffer descriptor of
+    // the rows from qi0 on: rows past the end read as zero (their
+    // probabilities are masked), and no lane holds a 64-bit address.  Every
+    // lane loads (no branch around loads); the values are used only when
+    // stored at the end of the step, so nothing waits for them before.
+    const uint32_t bytes = (uint32_t)(N - qi0) * 4u;
+    lraw = buffer_load_f32(LSE + (size_t)qh * N + qi0, bytes, 4u * l32);
+    draw = buffer_load_f32(drow + (size_t)qh * N + qi0, bytes, 4u * l32);
   };
   auto store_step = [&](int buf) {
     if (tid < BQ) {
-      Ls[buf][tid] = lpre;
-      Ds[buf][tid] = dpre;
+      Ls[buf][tid] = lraw * 1.4426950408889634f;
+      Ds[buf][tid] = draw;
     }
   };
   static_assert(SPW_Q >= 1, "each wave loads part of every tile");
