@@ -394,19 +394,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
   const int qw0 = qb * BR + 32 * wave;  // first query row of this wave
   const int myq = qw0 + l32;
   const bool q_ok = myq < N;
-  // Q and dO rows as the B operands of S^T = K Q^T and dP^T = V dO^T: lane
-  // holds row myq, columns 16 kk + 8 hh + 0..7.  Rows past the end are zero
-  // (with L = D = 0 their dS is exactly 0).
-  v8 qf[D / 16], dof[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const size_t off = hoff + (size_t)myq * D + 16 * kk + 8 * hh;
-    qf[kk] = q_ok ? ld16<v8>(Q + off) : v8{};
-    dof[kk] = q_ok ? ld16<v8>(dO + off) : v8{};
-  }
-  const float lq = q_ok ? LSE[(size_t)bh * N + myq] * 1.4426950408889634f : 0.f;
-  const float dq_row = q_ok ? drow[(size_t)bh * N + myq] : 0.f;
-
   f32x16 dqacc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) dqacc[i] = f32x16{};
@@ -428,16 +415,36 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
   const uint32_t rb = tile_row_base<D>(l32, hh);
   const uint32_t tb = tile_tr_base<D>(4 * hh + (li >> 2), 16 * (grp & 1) + 4 * (li & 3));
 
-  // Tiles 0 .. RING-2 in flight; wait for tile 0.
+  // Tiles 0 .. RING-2 start loading first, then the rows of Q, dO, L and D:
+  // scaling L waits for its load and, the counter being in order, for every
+  // load issued before it, so issued the other way round the tiles' loads
+  // would start only once the rows had arrived.
   load_kv(Kh, K0, kbase);
   load_kv(Vh, V0, kbase);
   if (RING > 2 && nt > 1) {
     load_kv(Kh, K1, kbase + BC);
     load_kv(Vh, V1, kbase + BC);
-    wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
-  } else {
-    wait_counts<FA_VMCNT_LGKM0(0)>();
   }
+  asm volatile("" ::: "memory");  // keeps the row loads after the tiles' loads
+  // Q and dO rows as the B operands of S^T = K Q^T and dP^T = V dO^T: lane
+  // holds row myq, columns 16 kk + 8 hh + 0..7.  Rows past the end are zero
+  // (with L = D = 0 their dS is exactly 0).
+  v8 qf[D / 16], dof[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const size_t off = hoff + (size_t)myq * D + 16 * kk + 8 * hh;
+    qf[kk] = q_ok ? ld16<v8>(Q + off) : v8{};
+    dof[kk] = q_ok ? ld16<v8>(dO + off) : v8{};
+  }
+  const float lq = q_ok ? LSE[(size_t)bh * N + myq] * 1.4426950408889634f : 0.f;
+  const float dq_row = q_ok ? drow[(size_t)bh * N + myq] : 0.f;
+
+  // Wait for tile 0 (the row loads are younger than tile 1's, so with tile 1
+  // in flight this also waits for part of it).
+  if (RING > 2 && nt > 1)
+    wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
+  else
+    wait_counts<FA_VMCNT_LGKM0(0)>();
   bare_barrier();
 
   // One tile: tile j + RING - 1 starts loading into the buffer tile j-1 used,
