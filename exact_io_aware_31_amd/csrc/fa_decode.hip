@@ -501,7 +501,11 @@ __global__ __launch_bounds__(DGM_WAVES * 64) void decode_group_kernel(
   }
 }
 
-// Kernel 2: one wave per head merges its chunk summaries.
+// Kernel 2: one wave per head merges its chunk summaries.  The partial
+// outputs of the first MERGE_PRE chunks are loaded together with the chunks'
+// log-sum-exps, before their maximum is known, so that a merge of up to that
+// many chunks waits for memory once.
+constexpr int MERGE_PRE = 16;
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
@@ -510,21 +514,42 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   const int bh = blockIdx.x, lane = threadIdx.x;
   const float* __restrict__ pl = part_lse + (size_t)bh * splits;
   const float* __restrict__ po = part_o + (size_t)bh * splits * D;
-  float big = -INFINITY;
-  for (int s = lane; s < splits; s += 64) big = fmaxf(big, pl[s]);
+  constexpr int PER = D / 64;
+  // Chunks past the last read the last one again (no branch around the
+  // loads); their values are never used.
+  float pre[MERGE_PRE][PER];
+#pragma unroll
+  for (int s = 0; s < MERGE_PRE; ++s)
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      pre[s][i] = po[(size_t)min(s, splits - 1) * D + lane + 64 * i];
+  // Lane s holds the log-sum-exp of chunk s (of the first 64).
+  const float lsev = lane < splits ? pl[lane] : -INFINITY;
+  float big = lsev;
+  for (int s = lane + 64; s < splits; s += 64) big = fmaxf(big, pl[s]);
   big = wave_max(big);
   if (big == -INFINITY) {  // no key at all (an empty history): O = 0, lse = -inf
     for (int i = lane; i < D; i += 64) O[(size_t)bh * D + i] = (T)0.f;
     if (LSE && lane == 0) LSE[bh] = -INFINITY;
     return;
   }
-  constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float wsum = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float w = expf(pl[s] - big);  // exp(-inf) = 0 for empty chunks
+  static_assert(MERGE_PRE <= 64, "the prefetched chunks' log-sum-exps are lanes of one wave");
+#pragma unroll
+  for (int s = 0; s < MERGE_PRE; ++s) {
+    if (s < splits) {
+      const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsev), s));
+      const float w = expf(ls - big);  // exp(-inf) = 0 for empty chunks
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, pre[s][i], acc[i]);
+    }
+  }
+  for (int s = MERGE_PRE; s < splits; ++s) {
+    const float w = expf(pl[s] - big);
     wsum += w;
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, po[(size_t)s * D + lane + 64 * i], acc[i]);
