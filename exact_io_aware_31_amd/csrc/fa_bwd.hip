@@ -439,8 +439,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
   const float lq = q_ok ? LSE[(size_t)bh * N + myq] * 1.4426950408889634f : 0.f;
   const float dq_row = q_ok ? drow[(size_t)bh * N + myq] : 0.f;
 
-  // Wait for tile 0 (the row loads are younger than tile 1's, so with tile 1
-  // in flight this also waits for part of it).
+  // Wait for tile 0.  The row loads are younger than tile 1's, so in a wave
+  // that loads rows this also waits for tile 1.
   if (RING > 2 && nt > 1)
     wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
   else

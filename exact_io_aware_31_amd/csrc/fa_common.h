@@ -74,6 +74,20 @@ __device__ __forceinline__ void wait_counts() {
   __builtin_amdgcn_s_waitcnt(IMM);
   asm volatile("" ::: "memory");
 }
+// Makes the kernel arguments given load at the kernel's start.  The compiler
+// loads an argument with a scalar load just before its first use; one still
+// outstanding when a kernel's main loop starts makes it wait for every LDS
+// read at the first LDS wait of each iteration (scalar and LDS loads share
+// one counter, and scalar loads may return out of order).
+template <typename X>
+__device__ __forceinline__ void load_arg_now(X x) {
+  asm volatile("" ::"s"(x));
+}
+template <typename... A>
+__device__ __forceinline__ void load_args_now(A... a) {
+  (load_arg_now(a), ...);
+}
+
 // Workgroup barrier without the memory fence of __syncthreads() (the fence
 // waits for every outstanding memory operation of the wave, including loads
 // issued for later tiles); the memory clobbers keep every LDS access on its
