@@ -357,11 +357,12 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
 
 // ---------------------------------------------------------------- kernel 3
 // NW waves x 32 query rows per workgroup: eight waves (one workgroup per CU,
-// a three-deep ring) by default, four (two workgroups per CU, a two-deep
-// ring) when the grid of 256-row blocks is small, as in the forward pass.
+// a three-deep ring) or four (two workgroups per CU, a two-deep ring); the
+// launcher picks by the number of 256-row blocks.
 constexpr int DQ_BC = 64;  // keys per tile
 constexpr int DQ_READ_AHEAD = 6;  // S / dP MFMAs whose LDS operands are read ahead
-constexpr long DQ_SMALL_GRID = 256;  // 256-row blocks below which dQ runs four-wave workgroups
+constexpr long DQ_SMALL_GRID = 256;   // 256-row blocks below which dQ runs four-wave workgroups
+constexpr long DQ_LARGE_GRID = 1024;  // ... and from which on it runs them again
 
 template <typename T, int D, bool CAUSAL, bool WIN, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
@@ -609,15 +610,19 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
                     kv_total, group, window, a.scale, c);
   if (e != hipSuccess) return e;
 
-  // dQ: fewer 256-row blocks than CUs: four-wave workgroups, two per CU.
-  // (With the rank-major work order, eight-wave ones win from one block per
-  // CU on: B2 H16 N4096, 512 blocks, 0.4699 ms with four-wave workgroups,
-  // 0.4669 with eight-wave ones; gradients bitwise identical.)
-  const bool small = (long)a.B * a.H * ((a.N + 255) / 256) < DQ_SMALL_GRID;
-  const int br = small ? 128 : 256;
+  // dQ: four-wave workgroups, two per CU, below one 256-row block per CU and
+  // from four per CU on; eight-wave ones in between.  Measured, gradients
+  // bitwise identical (eight-wave against four-wave): 512 blocks, B2 H16
+  // N4096 0.4509 / 0.4533 ms and B1 H16 N16384 3.3205 / 3.3228; 1024
+  // blocks, B1 H32 N8192 1.6776 / 1.6619 and B8 H16 N2048 0.5229 / 0.5103;
+  // 2048 blocks, B4 H32 N4096 1.8679 / 1.8611 and B2 H32 N8192 3.4116 /
+  // 3.3883.
+  const long blocks256 = (long)a.B * a.H * ((a.N + 255) / 256);
+  const bool four_wave = blocks256 < DQ_SMALL_GRID || blocks256 >= DQ_LARGE_GRID;
+  const int br = four_wave ? 128 : 256;
   const int nqb = (a.N + br - 1) / br;
   const int dq_total = a.B * a.H * nqb;
-  if (small)
+  if (four_wave)
     return launch_kernel(bwd_dq_kernel<T, D, CAUSAL, WIN, 4>, dim3(dq_total), dim3(4 * 64), s, q, k,
                          v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
                          window, a.scale, c);

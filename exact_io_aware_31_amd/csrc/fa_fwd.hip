@@ -11,9 +11,9 @@
 //
 // MI355X mapping (not the pages' A100 tile rule):
 //   * NW waves x 32 query rows per workgroup, two waves per SIMD; 64-key
-//     tiles.  Eight-wave workgroups (one per CU) are the default; when the
-//     grid of 256-row blocks is too small to give every CU several of them,
-//     four-wave workgroups run two per CU instead.
+//     tiles.  Eight-wave workgroups (one per CU) are the default; for small
+//     grids and short sequences four-wave workgroups run two per CU instead
+//     (the rule and its measurements are at the launcher).
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
 //     each lane then owns ONE query row per 32-row group (column l % 32) and
 //     16 of its scores per 32-key block, so the row max / row sum are in-lane
@@ -380,13 +380,22 @@ static hipError_t launch_fwd_nw(const FwdArgs& a, hipStream_t s) {
                        a.H / a.Hkv, WIN ? a.window : 0, c);
 }
 
-// Fewer than four 256-row blocks per CU (1024 on the 256 CUs): four-wave
-// workgroups, two per CU, keep the SIMDs fed.  Measured, interleaved on one
-// box (outputs bitwise identical): B4 H16 N2048 causal 0.0795 ms against
-// 0.0805 with eight-wave workgroups; at B1 H32 N8192, 1024 blocks, the
-// eight-wave shape is faster, 0.4950 against 0.5004 ms, as its K/V tiles
-// serve twice the rows.
-constexpr long FWD_SMALL_GRID = 1024;
+// Four-wave workgroups (two per CU) when the grid of 256-row blocks gives
+// at most one per CU, or when blocks are short (N <= 2048) and there are at
+// most four per CU; eight-wave workgroups otherwise, whose K/V tiles serve
+// twice the rows.  Measured causal, interleaved on one box, eight-wave
+// against four-wave (outputs bitwise identical):
+//   256 blocks:  B1 H16 N4096 0.1075 / 0.0871 ms, B1 H8 N8192 0.1907 / 0.1596,
+//                B4 H16 N1024 0.0333 / 0.0282;
+//   512 blocks:  B4 H16 N2048 0.0792 / 0.0783, B2 H16 N4096 0.1350 / 0.1427,
+//                B1 H16 N8192 0.2573 / 0.2726;
+//   1024 blocks: B16 H16 N1024 0.1069 / 0.0993, B8 H16 N2048 0.1616 / 0.1471,
+//                B4 H16 N4096 0.2754 / 0.2646, B1 H32 N8192 0.5135 / 0.5227;
+//   2048 blocks: B16 H16 N2048 0.3373 / 0.3415, B4 H32 N4096 0.5635 / 0.5666,
+//                B2 H32 N8192 1.0260 / 1.0452, B1 H32 N16384 1.9348 / 1.9684.
+constexpr long FWD_ONE_PER_CU = 256;
+constexpr long FWD_FOUR_PER_CU = 1024;
+constexpr int FWD_SHORT_N = 2048;
 
 // A sliding window of up to 2048 keys bounds each block's work to a few
 // tiles, so the smaller blocks win there too (window 1024 at B1 H32 N8192:
@@ -396,7 +405,9 @@ constexpr int FWD_SMALL_WINDOW = 2048;
 template <typename T, int D, bool CAUSAL, bool WIN>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const long blocks256 = (long)a.B * a.H * ((a.N + 255) / 256);
-  const bool small = blocks256 < FWD_SMALL_GRID || (WIN && a.window <= FWD_SMALL_WINDOW);
+  const bool small = blocks256 <= FWD_ONE_PER_CU ||
+                     (a.N <= FWD_SHORT_N && blocks256 <= FWD_FOUR_PER_CU) ||
+                     (WIN && a.window <= FWD_SMALL_WINDOW);
   return small ? launch_fwd_nw<T, D, CAUSAL, WIN, 4>(a, s) : launch_fwd_nw<T, D, CAUSAL, WIN, 8>(a, s);
 }
 

@@ -180,11 +180,13 @@ def test_fwd_ex_both_workgroup_shapes(B, H, N, window):
         check_max_abs(lse_h[b, h], lse_ref, dtype, f"lse head ({b},{h})")
 
 
-@pytest.mark.parametrize("B,H,N,window", [(2, 28, 1024, 300), (2, 64, 2304, 2100)],
-                         ids=["4wave-dq", "8wave-dq"])
+@pytest.mark.parametrize("B,H,N,window", [(2, 28, 1024, 300), (2, 32, 2304, 2100),
+                                          (2, 64, 2304, 2100)],
+                         ids=["4wave-dq", "8wave-dq", "4wave-dq-large"])
 def test_bwd_ex_both_dq_shapes(B, H, N, window):
-    """Grouped heads and a window in the backward at a dQ grid under (4-wave: 224) and over
-    (8-wave: 1152) 256 blocks of 256 rows; whole key/value groups against the oracle."""
+    """Grouped heads and a window in the backward at dQ grids of 224 (four-wave workgroups),
+    576 (eight-wave) and 1152 (four-wave) blocks of 256 rows: the dQ pass runs four-wave
+    workgroups below 256 blocks and from 1024 on.  Whole key/value groups against the oracle."""
     d, dtype = 128, torch.bfloat16
     Hkv = H // 4
     seed = 9960 + H

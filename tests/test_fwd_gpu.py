@@ -95,10 +95,11 @@ def test_fwd_deterministic():
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-@pytest.mark.parametrize("H", [63, 64], ids=["4wave", "8wave"])
+@pytest.mark.parametrize("H", [64, 65], ids=["4wave", "8wave"])
 def test_fwd_both_workgroup_shapes(H, causal, d, dtype):
-    """B4 N1024: 64 heads give 1024 blocks of 256 rows (eight-wave workgroups), 63 heads 1008
-    (four-wave workgroups, two per CU).  Whole heads spread over the grid against the oracle."""
+    """B4 N1024: 64 heads give 1024 blocks of 256 rows, the most that blocks of N <= 2048 run
+    as four-wave workgroups (two per CU); 65 heads give 1040 and run eight-wave ones.  Whole
+    heads spread over the grid against the oracle."""
     B, N = 4, 1024
     seed = 7300 + H + d + (1 if causal else 0)
     announce(f"fwd shapes B{B} H{H} N{N} d{d} causal={causal} {dtype} seed={seed}")

@@ -14,10 +14,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.mark.parametrize("H,causal", [(4, True), (2, False)], ids=["8wave-causal", "4wave-full"])
+@pytest.mark.parametrize("H,causal", [(4, True), (1, False)], ids=["8wave-causal", "4wave-full"])
 def test_fwd_long_sequence(H, causal):
     """B1 N65536 d128 bf16: 4 causal heads fill 1024 blocks of 256 rows (eight-wave
-    workgroups), 2 non-causal heads 512 (four-wave workgroups)."""
+    workgroups), 1 non-causal head 256 (four-wave workgroups, two per CU)."""
     B, N, d, dtype = 1, 65536, 128, torch.bfloat16
     seed = 9200 + H
     announce(f"fwd long B{B} H{H} N{N} d{d} causal={causal} seed={seed}")

@@ -78,11 +78,11 @@ def run_fwd(q, k, v, scale, causal, window):
     return o, lse
 
 
-# (mask, workgroup shape) -> (B, H, N, window): the launcher takes eight-wave workgroups from
-# 1024 blocks of 256 query rows on, four-wave ones below, and four-wave ones for any window of
-# up to 2048 keys.
-SHAPES = {("full", "4wave"): (1, 2, 512, 0), ("full", "8wave"): (2, 256, 512, 0),
-          ("causal", "4wave"): (1, 2, 512, 0), ("causal", "8wave"): (2, 256, 512, 0),
+# (mask, workgroup shape) -> (B, H, N, window): the launcher takes four-wave workgroups for at
+# most 256 blocks of 256 query rows, for N <= 2048 up to 1024 blocks, and for any window of up
+# to 2048 keys; eight-wave ones otherwise.
+SHAPES = {("full", "4wave"): (1, 2, 512, 0), ("full", "8wave"): (2, 264, 512, 0),
+          ("causal", "4wave"): (1, 2, 512, 0), ("causal", "8wave"): (2, 264, 512, 0),
           ("window", "4wave"): (1, 2, 1024, 300), ("window", "8wave"): (1, 64, 4096, 2500)}
 
 
