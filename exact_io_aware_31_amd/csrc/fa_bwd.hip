@@ -11,8 +11,9 @@
 //     dS = P o (dP - D)                     dK = scale dS^T Q,  dQ = scale dS K
 // (D_i equals sum_j P_ij dP_ij because each row of O is P_i V.)
 //
-// Three kernels on one stream, none of which uses atomics (every output
-// element is written once, by one lane, so the results are deterministic):
+// Three kernels, none of which uses atomics (every output element is written
+// once, by one lane, so the results are deterministic); on small grids the
+// third runs on a second stream beside the second (see the launchers):
 //   1. bwd_pre: D = rowsum(dO o O) in fp32.
 //   2. bwd_kv:  dK and dV.  One workgroup of 4 waves per block of 128 keys;
 //      wave w owns 32 keys and keeps V_w and its dK, dV accumulators in
@@ -39,6 +40,8 @@
 // LDS tiles use the forward's unpadded, swizzled layout (fa_tile.h: 16-byte
 // row reads and transpose reads conflict-free) and are filled by direct
 // buffer-to-LDS loads (TileLoader).
+#include <mutex>
+
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -587,6 +590,68 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
+// On small grids the dQ pass runs on a second stream beside the dK/dV pass
+// (both read only what bwd_pre wrote): each pass alone leaves most CUs idle
+// while its heaviest blocks finish.  The caller's stream forks to the second
+// stream after bwd_pre and joins it after the dQ pass, through two events,
+// so work later queued on the caller's stream still follows the whole
+// backward; kernels and results are the same as on one stream.  Measured
+// against one stream (causal unless noted, d = 128, blocks of 128 keys):
+// B1 H4 N2048 (64 blocks) 0.1158 -> 0.0827 ms, B1 H8 N2048 0.1185 ->
+// 0.0902, B1 H4 N8192 (256) 0.4312 -> 0.3157, B4 H8 N1024 0.0705 -> 0.0654,
+// B1 H8 N4096 non-causal 0.2475 -> 0.2193, B1 H32 N2048 (512) 0.1658 ->
+// 0.1492, B1 H16 N4096 0.3063 -> 0.2624, B1 H64 N1024 0.0964 -> 0.0950; from
+// 1024 blocks on it loses: B4 H16 N2048 0.2571 -> 0.2631, B2 H16 N4096
+// 0.4596 -> 0.4656, B8 H16 N1024 0.1587 -> 0.1664, B1 H32 N8192 1.663 ->
+// 1.685.
+constexpr long BWD_SIDE_MAX_BLOCKS = 512;
+
+namespace {
+// The second stream and the fork / join events of one device, created on
+// the first small-grid call on it (never inside a stream capture) and kept
+// until the process ends.  The lock makes each call's fork, launches and
+// join one unit, so concurrent calls on one device never pair one call's
+// event with another's wait (they share the second stream and run its dQ
+// passes in order).
+struct SideStream {
+  hipStream_t s2;
+  hipEvent_t fork, join;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxSideDevices];
+
+// The current device's set, or null for one stream: s belongs to another
+// device, or the set does not exist yet and s is capturing.  Called with
+// g_side_mu held.
+hipError_t side_stream(hipStream_t s, SideStream*& out) {
+  out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  hipDevice_t sdev = -1;
+  if ((e = hipStreamGetDevice(s, &sdev)) != hipSuccess) return e;
+  if (sdev != dev || dev < 0 || dev >= kMaxSideDevices) return hipSuccess;
+  SideStream& ss = g_side[dev];
+  if (!ss.s2) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(s, &st)) != hipSuccess) return e;
+    if (st != hipStreamCaptureStatusNone) return hipSuccess;
+    SideStream n{};
+    if ((e = hipStreamCreateWithFlags(&n.s2, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess) {
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      (void)hipStreamDestroy(n.s2);
+      return e;
+    }
+    ss = n;
+  }
+  out = &ss;
+  return hipSuccess;
+}
+}  // namespace
+
 template <typename T, int D, bool CAUSAL, bool WIN>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.H * a.N;
@@ -605,6 +670,17 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int window = WIN ? a.window : 0;
   const int nkb = (a.N + KV_BK - 1) / KV_BK;
   const int kv_total = a.B * a.Hkv * nkb;
+
+  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  if (kv_total <= BWD_SIDE_MAX_BLOCKS) {
+    lock.lock();
+    if ((e = side_stream(s, side)) != hipSuccess) return e;
+    if (side) {
+      if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(side->s2, side->fork, 0)) != hipSuccess) return e;
+    }
+  }
   e = launch_kernel(bwd_kv_kernel<T, D, CAUSAL, WIN>, dim3(kv_total), dim3(KV_WAVES * 64), s, q, k,
                     v, dout, a.lse, a.drow, static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, nkb,
                     kv_total, group, window, a.scale, c);
@@ -622,13 +698,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int br = four_wave ? 128 : 256;
   const int nqb = (a.N + br - 1) / br;
   const int dq_total = a.B * a.H * nqb;
+  const hipStream_t sq = side ? side->s2 : s;
   if (four_wave)
-    return launch_kernel(bwd_dq_kernel<T, D, CAUSAL, WIN, 4>, dim3(dq_total), dim3(4 * 64), s, q, k,
-                         v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
-                         window, a.scale, c);
-  return launch_kernel(bwd_dq_kernel<T, D, CAUSAL, WIN, 8>, dim3(dq_total), dim3(8 * 64), s, q, k, v,
-                       dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
-                       window, a.scale, c);
+    e = launch_kernel(bwd_dq_kernel<T, D, CAUSAL, WIN, 4>, dim3(dq_total), dim3(4 * 64), sq, q, k,
+                      v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
+                      window, a.scale, c);
+  else
+    e = launch_kernel(bwd_dq_kernel<T, D, CAUSAL, WIN, 8>, dim3(dq_total), dim3(8 * 64), sq, q, k,
+                      v, dout, a.lse, a.drow, static_cast<T*>(a.dq), a.N, nqb, dq_total, group,
+                      window, a.scale, c);
+  if (e != hipSuccess || !side) return e;
+  if ((e = hipEventRecord(side->join, side->s2)) != hipSuccess) return e;
+  return hipStreamWaitEvent(s, side->join, 0);
 }
 
 template <typename T, int D>
