@@ -2,7 +2,9 @@
 //
 // Every argument is checked here, before any HIP call, so error paths can be
 // exercised on a machine without a GPU.  The launchers (fa_fwd.hip,
-// fa_bwd.hip, fa_decode.hip) only enqueue kernels on the caller's stream.
+// fa_bwd.hip, fa_decode.hip) only enqueue kernels on the caller's stream
+// (on small grids the backward also on a second stream of its own, forked
+// from and joined back into the caller's).
 #include "../../include/fa.h"
 
 #include <hip/hip_runtime.h>
