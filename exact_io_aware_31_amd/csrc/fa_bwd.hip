@@ -590,9 +590,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
-// On small grids the dQ pass runs on a second stream beside the dK/dV pass
-// (both read only what bwd_pre wrote): each pass alone leaves most CUs idle
-// while its heaviest blocks finish.  The caller's stream forks to the second
+// On small grids, and with grouped key/value heads, the dQ pass runs on a
+// second stream beside the dK/dV pass (both read only what bwd_pre wrote):
+// each pass alone leaves most CUs idle while its heaviest blocks finish, and
+// grouped heads make the dK/dV blocks long (each walks every query head of
+// its group).  The caller's stream forks to the second
 // stream after bwd_pre and joins it after the dQ pass, through two events,
 // so work later queued on the caller's stream still follows the whole
 // backward; kernels and results are the same as on one stream.  Measured
@@ -603,7 +605,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
 // 0.1492, B1 H16 N4096 0.3063 -> 0.2624, B1 H64 N1024 0.0964 -> 0.0950; from
 // 1024 blocks on it loses: B4 H16 N2048 0.2571 -> 0.2631, B2 H16 N4096
 // 0.4596 -> 0.4656, B8 H16 N1024 0.1587 -> 0.1664, B1 H32 N8192 1.663 ->
-// 1.685.
+// 1.685.  Grouped heads (H / H_kv query heads per key/value head): B1 H32
+// H_kv8 N8192 (512) 2.031 -> 1.715, B2 H16 H_kv4 N4096 (256) 0.7213 ->
+// 0.5861, and past 512 blocks B2 H32 H_kv8 N8192 (1024) 3.518 -> 3.373,
+// B2 H16 H_kv8 N8192 (1024) 1.761 -> 1.697, B4 H32 H_kv8 N4096 (1024) 1.823
+// -> 1.761, B8 H32 H_kv8 N2048 (2048) 0.9832 -> 0.9678.
 constexpr long BWD_SIDE_MAX_BLOCKS = 512;
 
 namespace {
@@ -673,7 +679,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
 
   std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
   SideStream* side = nullptr;
-  if (kv_total <= BWD_SIDE_MAX_BLOCKS) {
+  if (kv_total <= BWD_SIDE_MAX_BLOCKS || group > 1) {
     lock.lock();
     if ((e = side_stream(s, side)) != hipSuccess) return e;
     if (side) {

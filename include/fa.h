@@ -37,19 +37,20 @@
  *     float32 pointers 4-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work and return; errors during execution surface at the
- *     caller's next synchronisation.  fa_bwd on small grids runs one of its
- *     kernels on a second stream of the library's, forked from `stream` and
- *     joined back into it with events, so the call is still ordered on
- *     `stream` as a whole (also inside a stream capture); with a stream of
- *     a device other than the current one it uses `stream` alone.
+ *     caller's next synchronisation.  fa_bwd on small grids (and fa_bwd_ex
+ *     with grouped heads) runs one of its kernels on a second stream of the
+ *     library's, forked from `stream` and joined back into it with events,
+ *     so the call is still ordered on `stream` as a whole (also inside a
+ *     stream capture); with a stream of a device other than the current
+ *     one it uses `stream` alone.
  *   - Ownership: the caller allocates and owns every buffer, including the
  *     workspaces sized by the *_workspace_bytes queries.  The library never
  *     allocates or frees device memory.  The state it keeps, per device and
  *     until the process ends: the device address of fa_decode_noalloc's
  *     static scratch, looked up on its first call; fa_bwd's second stream
- *     and two events, created on its first small-grid call outside a stream
- *     capture (a capture before that runs the backward on `stream` alone).
- *     Outputs must not alias inputs.
+ *     and two events, created on the first call that uses them outside a
+ *     stream capture (a capture before that runs the backward on `stream`
+ *     alone).  Outputs must not alias inputs.
  *   - Errors: every argument is validated before any HIP call; on a
  *     validation error (every code but FA_ERR_HIP) nothing is enqueued and
  *     no output is touched.  FA_ERR_HIP means the runtime refused a kernel
@@ -115,7 +116,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  * Every output element is written once, without atomics: results are
  * deterministic (bitwise equal across runs with the same inputs).  For
  * grids of at most 512 blocks of 128 keys (B * H * ceil(N / 128)) the dQ
- * kernel runs on the library's second stream, beside the dK/dV kernel.
+ * kernel runs on the library's second stream, beside the dK/dV kernel (in
+ * fa_bwd_ex also whenever H_kv < H).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dout, void* dq, void* dk, void* dv,

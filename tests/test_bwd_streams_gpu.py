@@ -7,7 +7,9 @@ after the dQ kernel.  These tests check the ordering that promises:
   * calls from two host threads, on two streams of one device, each pair their own fork and
     join (the outputs of every call equal a lone call's, bitwise);
   * a backward captured into a graph before the library has made its second stream (a fresh
-    process) runs on the capturing stream alone, and its replays equal the eager result.
+    process) runs on the capturing stream alone, and its replays equal the eager result;
+  * grouped key/value heads, which take the second stream at any grid size, past 512 blocks
+    (against the oracle on sampled groups).
 The kernels are the same on one or two streams, so every comparison is bitwise.
 """
 import os
@@ -19,8 +21,9 @@ import pytest
 import torch
 
 import exact_io_aware_31_amd as fa
+import oracle
 from synth_inputs import attention_inputs
-from tests.parity_util import announce
+from tests.parity_util import announce, check_rel_norm, check_rel_norm_blocks, host64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -136,3 +139,25 @@ def test_capture_before_the_second_stream_exists():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "fresh capture ok" in r.stdout, (r.stdout[-2000:],
                                                                   r.stderr[-2000:])
+
+
+def test_grouped_heads_past_512_blocks():
+    """B32 H4 H_kv2 N1152 causal: 576 blocks of 128 keys, grouped heads, so the dQ pass runs
+    beside the dK/dV pass; sampled key/value groups against the oracle."""
+    B, H, Hkv, N, d, dtype, seed = 32, 4, 2, 1152, 128, torch.bfloat16, 9993
+    announce(f"bwd grouped two streams B{B} H{H} Hkv{Hkv} N{N} d{d} seed={seed}")
+    q, k, v, do = attention_inputs(B, H, N, d, dtype, seed, "cpu", with_dout=True, Hkv=Hkv)
+    scale = d ** -0.5
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = fa.attention_fwd(qd, kd, vd, scale, True)
+    dq, dk, dv = fa.attention_bwd(qd, kd, vd, o, lse, dod, scale, True)
+    torch.cuda.synchronize()
+    dq_h, dk_h, dv_h = host64(dq), host64(dk), host64(dv)
+    g = H // Hkv
+    for b, hk in [(0, 0), (17, 1), (B - 1, Hkv - 1)]:
+        hs = slice(g * hk, g * hk + g)
+        ref = oracle.attn_bwd(q[b, hs], k[b, hk:hk + 1], v[b, hk:hk + 1], do[b, hs], scale, True)
+        for name, gt, r in (("dQ", dq_h[b, hs], ref[0]), ("dK", dk_h[b, hk:hk + 1], ref[1]),
+                            ("dV", dv_h[b, hk:hk + 1], ref[2])):
+            check_rel_norm(gt, r, dtype, f"{name} group ({b},{hk})")
+            check_rel_norm_blocks(gt, r, dtype, f"{name} group ({b},{hk})")
