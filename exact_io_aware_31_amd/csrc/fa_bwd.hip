@@ -698,9 +698,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   // N4096 0.4509 / 0.4533 ms and B1 H16 N16384 3.3205 / 3.3228; 1024
   // blocks, B1 H32 N8192 1.6776 / 1.6619 and B8 H16 N2048 0.5229 / 0.5103;
   // 2048 blocks, B4 H32 N4096 1.8679 / 1.8611 and B2 H32 N8192 3.4116 /
-  // 3.3883.
+  // 3.3883.  Beside the dK/dV pass without grouped heads (at most 256 such
+  // blocks), four-wave workgroups share CUs with dK/dV ones, where the
+  // eight-wave ones do not fit beside them: at 256 blocks B1 H32 N2048
+  // 0.1538 -> 0.1448 ms, B1 H16 N4096 0.2725 -> 0.2522, B1 H64 N1024 0.0978
+  // -> 0.0923.  With grouped heads the rule stands (B2 H16 H_kv4 N4096,
+  // 512 blocks: 0.5912 eight-wave against 0.6672 four-wave).
   const long blocks256 = (long)a.B * a.H * ((a.N + 255) / 256);
-  const bool four_wave = blocks256 < DQ_SMALL_GRID || blocks256 >= DQ_LARGE_GRID;
+  const bool four_wave = blocks256 < DQ_SMALL_GRID || blocks256 >= DQ_LARGE_GRID ||
+                         (side && group == 1);
   const int br = four_wave ? 128 : 256;
   const int nqb = (a.N + br - 1) / br;
   const int dq_total = a.B * a.H * nqb;
