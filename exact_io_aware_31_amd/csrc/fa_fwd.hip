@@ -12,8 +12,12 @@
 // MI355X mapping (not the pages' A100 tile rule):
 //   * NW waves x 32 query rows per workgroup, two waves per SIMD; 64-key
 //     tiles.  Eight-wave workgroups (one per CU) are the default; for small
-//     grids and short sequences four-wave workgroups run two per CU instead
-//     (the rule and its measurements are at the launcher).
+//     grids and short sequences four-wave workgroups run two per CU instead.
+//     On grids of at most one 64-row block per CU, a four-wave workgroup
+//     takes 64 rows and its two pairs of waves split the keys (even and odd
+//     tiles of each step, merged at the end), so the longest block's tiles
+//     are shared by two waves (the rules and their measurements are at the
+//     launcher).
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
 //     each lane then owns ONE query row per 32-row group (column l % 32) and
 //     16 of its scores per 32-key block, so the row max / row sum are in-lane
@@ -63,7 +67,7 @@ constexpr int FWD_BC = 64;
 constexpr float FWD_RESCALE_SLACK = 8.0f;  // log2 units
 
 
-template <typename T, int D, bool CAUSAL, bool WIN, int NW, int QG>
+template <typename T, int D, bool CAUSAL, bool WIN, int NW, int QG, int KS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, int group, int window,
@@ -77,14 +81,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   // load at the start (load_args_now): B4 H16 N2048 +1.4 to +2.0%, bitwise
   // identical.  The eight-wave shape measured 0.6-0.8% slower with them.
   if constexpr (NW == 4) load_args_now(O, LSE, c);
-  constexpr int BR = NW * 32 * QG, BC = FWD_BC;
+  // KS = 2 splits the keys inside the workgroup (tiny grids): waves w and
+  // w + NW / 2 own the same 32 rows and take the even and the odd key tiles
+  // of each step, then merge their partial results at the end.
+  static_assert(KS == 1 || (KS == 2 && NW == 4), "key split only in four-wave workgroups");
+  constexpr int BR = NW * 32 * QG / KS, BC = FWD_BC;
   constexpr int SPW = BC * D * 2 / 1024 / NW;  // tile load segments per wave (vmcnt units)
-  constexpr int RING = NW == 8 ? 3 : 2;         // tiles in the LDS ring
+  constexpr int RING = NW == 8 ? 3 : 2;         // steps in the LDS ring
   static_assert(NW == 8 || NW == 4, "one eight-wave or two four-wave workgroups per CU");
   // The ring of K and V tiles (separate arrays, so every access names its
-  // buffer statically and the compiler sees which loads it depends on).
-  __shared__ __attribute__((aligned(1024))) T K0[BC * D], K1[BC * D], K2[RING > 2 ? BC * D : 1];
-  __shared__ __attribute__((aligned(1024))) T V0[BC * D], V1[BC * D], V2[RING > 2 ? BC * D : 1];
+  // buffer statically and the compiler sees which loads it depends on); a
+  // slot holds the KS tiles of one step.
+  __shared__ __attribute__((aligned(1024))) T K0[KS * BC * D], K1[KS * BC * D],
+      K2[RING > 2 ? BC * D : 1];
+  __shared__ __attribute__((aligned(1024))) T V0[KS * BC * D], V1[KS * BC * D],
+      V2[RING > 2 ? BC * D : 1];
 
   // Work item: XCD-local heads, heaviest causal query blocks first.
   int bh, rank;
@@ -93,6 +104,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform_int(tid >> 6);  // wave-uniform
+  const int rg = wave % (NW / KS), kh = wave / (NW / KS);  // row group, key tile parity
   const int l32 = lane & 31, hh = lane >> 5;
   const size_t hoff = (size_t)bh * N * D;
   // Query head bh reads key/value head bh / group (groups of consecutive
@@ -102,7 +114,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   const T* __restrict__ Kh = K + kvoff;
   const T* __restrict__ Vh = V + kvoff;
 
-  const int qw0 = qb * BR + wave * 32 * QG;  // first query row of this wave
+  const int qw0 = qb * BR + rg * 32 * QG;  // first query row of this wave
   int myq[QG];
 #pragma unroll
   for (int g = 0; g < QG; ++g) myq[g] = qw0 + 32 * g + l32;
@@ -136,13 +148,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   // tiles before the one holding it are never loaded.
   const int kbase = (CAUSAL && window > 0) ? (max(0, qb * BR - window + 1) / BC) * BC : 0;
   const int nt = ntiles - kbase / BC;  // tiles this workgroup streams
+  const int nst = (nt + KS - 1) / KS;   // steps (KS tiles each)
 
   // Tile loads (TileLoader): rows past the end read as zero; those keys are
   // masked to -inf before the softmax, so their probabilities (and their V
   // rows' weight) are 0.
   const TileLoader<D, BC, NW> loader(wave, lane);
   auto load_kv = [&](const T* __restrict__ src, T* dst, int kb) {
-    loader.load(src, N, kb, dst, wave);
+    if constexpr (KS == 1) {
+      loader.load(src, N, kb, dst, wave);  // kb < N
+    } else {
+      // A step's second tile can start past the end (an odd tile count):
+      // from N on, nothing is read and the slot fills with zeros.
+#pragma unroll
+      for (int s = 0; s < KS; ++s) loader.load(src, N, min(kb + s * BC, N), dst + s * BC * D, wave);
+    }
   };
   // Per-lane element offsets of the operand reads (the swizzle depends on the
   // row mod 16 only, so they hold for every 16- or 32-row block of a tile):
@@ -164,7 +184,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   // Tiles 0 .. RING-2 in flight; wait for tile 0 (vmcnt counts this wave's loads).
   load_kv(Kh, K0, kbase);
   load_kv(Vh, V0, kbase);
-  if (RING > 2 && nt > 1) {
+  if (RING > 2 && nst > 1) {
     load_kv(Kh, K1, kbase + BC);
     load_kv(Vh, V1, kbase + BC);
     wait_counts<FA_VMCNT_LGKM0(2 * SPW)>();
@@ -178,21 +198,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   // One tile: tile j + RING - 1 starts loading into the buffer tile j-1
   // used, tile j is computed, and before the barrier this wave's loads of
   // tile j+1 are done.
-  auto tile_step = [&](int j, const T* __restrict__ kt, const T* __restrict__ vt, T* kn, T* vn) {
-    const int kb = kbase + j * BC;
-    const bool more = j + RING - 1 < nt;
+  auto tile_step = [&](int j, const T* __restrict__ kslot, const T* __restrict__ vslot, T* kn,
+                       T* vn) {
+    const int kb0 = kbase + j * KS * BC;  // the step's first key
+    const bool more = j + RING - 1 < nst;
     if (more) {
-      load_kv(Kh, kn, kb + (RING - 1) * BC);
-      load_kv(Vh, vn, kb + (RING - 1) * BC);
+      load_kv(Kh, kn, kb0 + (RING - 1) * KS * BC);
+      load_kv(Vh, vn, kb0 + (RING - 1) * KS * BC);
     }
+    // This wave's tile of the step.
+    const int kb = kb0 + kh * BC;
+    const T* __restrict__ kt = kslot + kh * BC * D;
+    const T* __restrict__ vt = vslot + kh * BC * D;
     bool active[QG];
     bool any_active = false;
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
       // Causal: tiles wholly after the group's last row, or (window) wholly
       // before its first row's window, are skipped.
-      active[g] = !CAUSAL || (kb <= qw0 + 32 * g + 31 &&
-                              (window == 0 || kb + BC - 1 > qw0 + 32 * g - window));
+      active[g] = (KS == 1 || j * KS + kh < nt) &&
+                  (!CAUSAL || (kb <= qw0 + 32 * g + 31 &&
+                               (window == 0 || kb + BC - 1 > qw0 + 32 * g - window)));
       any_active |= active[g];
     }
     if (any_active) {
@@ -324,16 +350,48 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   };
   // Unrolled by the ring depth so each step names its ring buffers statically.
   if constexpr (RING == 3) {
-    for (int j = 0; j < nt; j += 3) {
+    for (int j = 0; j < nst; j += 3) {
       tile_step(j, K0, V0, K2, V2);
-      if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
-      if (j + 2 < nt) tile_step(j + 2, K2, V2, K1, V1);
+      if (j + 1 < nst) tile_step(j + 1, K1, V1, K0, V0);
+      if (j + 2 < nst) tile_step(j + 2, K2, V2, K1, V1);
     }
   } else {
-    for (int j = 0; j < nt; j += 2) {
+    for (int j = 0; j < nst; j += 2) {
       tile_step(j, K0, V0, K1, V1);
-      if (j + 1 < nt) tile_step(j + 1, K1, V1, K0, V0);
+      if (j + 1 < nst) tile_step(j + 1, K1, V1, K0, V0);
     }
+  }
+
+  if constexpr (KS == 2) {
+    // Merge the two key halves of each row group: the odd-tile wave leaves
+    // its reference maximum, its partial row sums and its output
+    // accumulators in a V slot (free after the last barrier), in its own
+    // lane order, and the even-tile wave of the same rows adds them in,
+    // both rescaled to the larger reference.
+    constexpr int NX = 2 + D / 32 * 16;  // floats per lane
+    static_assert(NX * 64 * 4 <= KS * BC * D * (int)sizeof(T), "partials fit in a V slot");
+    float* const xa = reinterpret_cast<float*>(rg == 0 ? V0 : V1);
+    if (kh == 1) {
+      xa[lane] = m_run[0];
+      xa[64 + lane] = l_run[0];
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xa[(2 + 16 * nb + r) * 64 + lane] = oacc[0][nb][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = xa[lane], l1 = xa[64 + lane];
+    const float m = fmaxf(m_run[0], m1);
+    const float a0 = (m == -INFINITY) ? 1.f : fast_exp2(m_run[0] - m);
+    const float a1 = (m == -INFINITY) ? 0.f : fast_exp2(m1 - m);
+    l_run[0] = l_run[0] * a0 + l1 * a1;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oacc[0][nb][r] = oacc[0][nb][r] * a0 + xa[(2 + 16 * nb + r) * 64 + lane] * a1;
+    m_run[0] = m;
   }
 
   // Epilogue: O = O / l, lse = (m + log2 l) ln 2.  The output goes through
@@ -344,6 +402,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   // wave stages its own 32 rows in half of one ring buffer.
   static_assert(QG == 1, "one 32-row group per wave");
   T* const stage = (wave < 2 ? K0 : wave < 4 ? K1 : wave < 6 ? K2 : V0) + (wave & 1) * 32 * D;
+  static_assert(KS == 1 || NW == 4, "with the key split, waves 0 and 1 stage their rows in K0");
   const float l_tot = half_pair_sum(l_run[0]);
   const float inv = 1.f / l_tot;
 #pragma unroll
@@ -368,13 +427,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_kernel(
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool WIN, int NW>
+template <typename T, int D, bool CAUSAL, bool WIN, int NW, int KS = 1>
 static hipError_t launch_fwd_nw(const FwdArgs& a, hipStream_t s) {
-  const int br = NW * 32 * FWD_QG;
+  const int br = NW * 32 * FWD_QG / KS;
   const int nqb = (a.N + br - 1) / br;
   const int total = a.B * a.H * nqb;
   const float c = a.scale * 1.4426950408889634f;
-  return launch_kernel(fwd_kernel<T, D, CAUSAL, WIN, NW, FWD_QG>, dim3(total), dim3(NW * 64), s,
+  return launch_kernel(fwd_kernel<T, D, CAUSAL, WIN, NW, FWD_QG, KS>, dim3(total), dim3(NW * 64), s,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.N, nqb, total,
                        a.H / a.Hkv, WIN ? a.window : 0, c);
@@ -402,8 +461,25 @@ constexpr int FWD_SHORT_N = 2048;
 // 0.1665 ms with eight-wave workgroups, 0.1483 with four-wave ones).
 constexpr int FWD_SMALL_WINDOW = 2048;
 
+// Grids of at most one 64-row block per CU: four-wave workgroups of 64 rows
+// whose two pairs of waves split each step's keys (KS = 2), so the longest
+// block's tiles are shared by two waves.  Each step then loads two tiles
+// (a 128 KiB ring at d = 128: one workgroup per CU).  Measured against the
+// four-wave shape, interleaved on one box (causal unless noted): B1 H8 N2048
+// 0.0362 -> 0.0290 ms, non-causal 0.0352 -> 0.0297, B1 H4 N4096 0.0651 ->
+// 0.0504, B1 H2 N8192 0.1246 -> 0.0985, B1 H16 N1024 0.0204 -> 0.0174, B1
+// H1 N256 0.0086 / 0.0088.  Past 256 blocks it mostly loses (a second round
+// of workgroups): B1 H16 N4096 0.0827 -> 0.1126, B1 H4 N8192 0.1263 ->
+// 0.1440, B1 H32 N1024 0.0210 -> 0.0233; non-causal B1 H16 N2048 0.0379 ->
+// 0.0548.  A window keeps the other shapes.
+constexpr long FWD_KEY_SPLIT_MAX = 256;
+
 template <typename T, int D, bool CAUSAL, bool WIN>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
+  if constexpr (!WIN) {
+    if ((long)a.B * a.H * ((a.N + 63) / 64) <= FWD_KEY_SPLIT_MAX)
+      return launch_fwd_nw<T, D, CAUSAL, WIN, 4, 2>(a, s);
+  }
   const long blocks256 = (long)a.B * a.H * ((a.N + 255) / 256);
   const bool small = blocks256 <= FWD_ONE_PER_CU ||
                      (a.N <= FWD_SHORT_N && blocks256 <= FWD_FOUR_PER_CU) ||

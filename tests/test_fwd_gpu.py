@@ -112,3 +112,26 @@ def test_fwd_both_workgroup_shapes(H, causal, d, dtype):
         o_ref, lse_ref = oracle.attn_fwd(q[b, h], k[b, h], v[b, h], scale, causal)
         check_max_abs(o_h[b, h], o_ref, dtype, f"O head ({b},{h})")
         check_max_abs(lse_h[b, h], lse_ref, dtype, f"lse head ({b},{h})")
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float16, 64)],
+                         ids=["bf16-d128", "f16-d64"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("H,N", [(4, 4096), (4, 4097), (2, 4000)],
+                         ids=["keysplit-256", "4wave-260", "keysplit-odd-tiles"])
+def test_fwd_key_split_boundary(H, N, causal, d, dtype):
+    """Grids of at most 256 blocks of 64 rows run four-wave workgroups whose two pairs of waves
+    split each step's keys and merge at the end: B1 H4 N4096 is 256 such blocks, N4097 is 260
+    and runs the plain four-wave shape; N4000 leaves an odd number of key tiles, so the last
+    step's second tile starts past the end.  Every head against the oracle."""
+    B = 1
+    seed = 7400 + H + N + d + (1 if causal else 0)
+    announce(f"fwd key split B{B} H{H} N{N} d{d} causal={causal} {dtype} seed={seed}")
+    q, k, v = attention_inputs(B, H, N, d, dtype, seed, "cpu")
+    scale = d ** -0.5
+    o, lse = run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal)
+    o_h, lse_h = host64(o), host64(lse)
+    for h in range(H):
+        o_ref, lse_ref = oracle.attn_fwd(q[0, h], k[0, h], v[0, h], scale, causal)
+        check_max_abs(o_h[0, h], o_ref, dtype, f"O head {h}")
+        check_max_abs(lse_h[0, h], lse_ref, dtype, f"lse head {h}")

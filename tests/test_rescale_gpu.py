@@ -78,22 +78,26 @@ def run_fwd(q, k, v, scale, causal, window):
     return o, lse
 
 
-# (mask, workgroup shape) -> (B, H, N, window): the launcher takes four-wave workgroups for at
-# most 256 blocks of 256 query rows, for N <= 2048 up to 1024 blocks, and for any window of up
-# to 2048 keys; eight-wave ones otherwise.
-SHAPES = {("full", "4wave"): (1, 2, 512, 0), ("full", "8wave"): (2, 264, 512, 0),
-          ("causal", "4wave"): (1, 2, 512, 0), ("causal", "8wave"): (2, 264, 512, 0),
+# (mask, workgroup shape) -> (B, H, N, window): without a window, the launcher takes four-wave
+# workgroups of 64 rows that split each step's keys between two pairs of waves for at most 256
+# blocks of 64 rows; four-wave workgroups of 128 rows for at most 256 blocks of 256 query rows,
+# for N <= 2048 up to 1024 blocks, and for any window of up to 2048 keys; eight-wave ones
+# otherwise.
+SHAPES = {("full", "keysplit"): (1, 2, 512, 0), ("full", "4wave"): (1, 40, 512, 0),
+          ("full", "8wave"): (2, 264, 512, 0),
+          ("causal", "keysplit"): (1, 2, 512, 0), ("causal", "4wave"): (1, 40, 512, 0),
+          ("causal", "8wave"): (2, 264, 512, 0),
           ("window", "4wave"): (1, 2, 1024, 300), ("window", "8wave"): (1, 64, 4096, 2500)}
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("mask", ["full", "causal", "window"])
-@pytest.mark.parametrize("shape", ["4wave", "8wave"])
+@pytest.mark.parametrize("mask,shape", sorted(SHAPES), ids=[f"{m}-{s}" for m, s in sorted(SHAPES)])
 def test_fwd_rescale_with_growing_maximum(shape, mask, d, dtype):
     B, H, N, window = SHAPES[(mask, shape)]
     causal = mask != "full"
-    seed = 9200 + d + 3 * (mask == "causal") + 5 * (mask == "window") + 7 * (shape == "8wave")
+    seed = 9200 + d + 3 * (mask == "causal") + 5 * (mask == "window") + 7 * (shape == "8wave") + \
+        11 * (shape == "keysplit")
     announce(f"fwd rescale {shape} {mask} B{B} H{H} N{N} d{d} window={window} {dtype} seed={seed}")
     q, k, v = ramp_inputs(B, H, N, d, dtype, seed)
     scale = d ** -0.5
