@@ -84,27 +84,36 @@ constexpr int KV_BK = 32 * KV_WAVES;  // keys per workgroup
 constexpr int KV_BQ = 32;             // query rows per step
 constexpr int KV_READ_AHEAD = 3;      // S / dP MFMAs whose LDS operands are read ahead
 
-template <typename T, int D, bool CAUSAL, bool WIN>
-__global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
+template <typename T, int D, bool CAUSAL, bool WIN, int QS>
+__global__ __launch_bounds__(KV_WAVES * 64, QS == 1 ? 2 : 1) void bwd_kv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ drow,
     T* __restrict__ dK, T* __restrict__ dV, int N, int nkb, int total, int group, int window,
     float scale, float c) {
   using v8 = typename Vec<T>::v8;
   if constexpr (!WIN) window = 0;  // window code only in the WIN instantiation
-  constexpr int BK = KV_BK, BQ = KV_BQ, NB = D / 32;
+  // QS = 2 splits the query steps inside the workgroup (tiny grids): waves w
+  // and w + 2 own the same 32 keys and take the even and the odd query step
+  // of each pair, then merge their dK and dV at the end; a block has 64 keys.
+  // Its Q / dO ring holds two query tiles per step (81 KiB of LDS at
+  // d = 128), so one such workgroup runs per CU, with registers to match.
+  static_assert(QS == 1 || QS == 2, "query steps split in two at most");
+  constexpr int KWAVES = KV_WAVES / QS;  // waves per set of the block's keys
+  constexpr int BK = 32 * KWAVES, BQ = KV_BQ, NB = D / 32;
   constexpr int SPW_Q = BQ * D * 2 / 1024 / KV_WAVES;  // load segments per wave per Q tile
-  __shared__ __attribute__((aligned(1024))) T Qs[2][BQ * D];
-  __shared__ __attribute__((aligned(1024))) T dOs[2][BQ * D];
+  __shared__ __attribute__((aligned(1024))) T Qs[2][QS * BQ * D];
+  __shared__ __attribute__((aligned(1024))) T dOs[2][QS * BQ * D];
   __shared__ __attribute__((aligned(1024))) T Ks[BK * D];  // this block's keys
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ls[2][QS * BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][QS * BQ];
 
   // Work item: XCD-local heads; causal key blocks heaviest (first) first.
   int kvbh, kblk;  // key/value head (over B x H_kv), key block
   work_item(blockIdx.x, total / nkb, nkb, CAUSAL && !WIN, kvbh, kblk);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform_int(tid >> 6);  // wave-uniform
+  const int kw = QS == 1 ? wave : wave % KWAVES;  // the wave's set of 32 keys
+  const int qp = QS == 1 ? 0 : wave / KWAVES;     // the wave's step of each pair
   const int l32 = lane & 31, hh = lane >> 5;
   const int li = lane & 15, grp = lane >> 4;
   // K, V, dK, dV of key/value head kvbh; the query heads of its group are
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   const T* __restrict__ Vh = V + hoff;
 
   const int kj0 = kblk * BK;
-  const int kw0 = kj0 + 32 * wave;  // first key of this wave
+  const int kw0 = kj0 + 32 * kw;  // first key of this wave
   const int mykey = kw0 + l32;      // the key this lane owns in S, dP, dS
   const bool key_ok = mykey < N;
 
@@ -143,7 +152,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   // 32x32 accumulator layout gives P and dS to the A operand.
   const uint32_t rb = tile_row_base<D>(l32, hh);
   const uint32_t tb = tile_tr_base<D>(4 * hh + (li >> 2), 16 * (grp & 1) + 4 * (li & 3));
-  const uint32_t kwb = rb + 64 * D * wave;  // this wave's 32 K rows: 32 D * 2 bytes per wave
+  const uint32_t kwb = rb + 64 * D * kw;  // this wave's 32 K rows: 32 D * 2 bytes per wave
 
   // Q and dO tiles of a step go straight into LDS buffer `buf` (rows past the
   // end read as zero, their probabilities masked to 0); L and D of the step's
@@ -165,52 +174,89 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   };
   float lraw = 0.f, draw = 0.f;
   const TileLoader<D, BQ, KV_WAVES> step_loader(wave, lane);
-  auto load_step = [&](int qh, int qi0, int buf) {
-    const size_t qoff = (size_t)qh * N * D;
-    // The direct loads name their ring slot through an opaque LDS address.
-    // Loads into a slot the compiler can trace (the Qs / dOs arrays) make it
-    // wait for them before every later read of the same array, including
-    // the reads of the other slot, which is this step's: the next step's
-    // tiles would have to arrive before this step could start.  The slots
-    // are ordered by the wait and the barrier that end every step instead.
-    step_loader.load(Q + qoff, N, qi0, opaque_lds(Qs[buf]), wave);
-    step_loader.load(dO + qoff, N, qi0, opaque_lds(dOs[buf]), wave);
-    // Rows qi0 + l32 of the head's L and D through a buffer descriptor of
-    // the rows from qi0 on: rows past the end read as zero (their
-    // probabilities are masked), and no lane holds a 64-bit address.  Every
-    // lane loads (no branch around loads); the values are used only when
-    // stored at the end of the step, so nothing waits for them before.
-    const uint32_t bytes = (uint32_t)(N - qi0) * 4u;
-    lraw = buffer_load_f32(LSE + (size_t)qh * N + qi0, bytes, 4u * l32);
-    draw = buffer_load_f32(drow + (size_t)qh * N + qi0, bytes, 4u * l32);
+  // Loads the QS query tiles of the steps from index si on (head qh, first
+  // row qi0) into ring slot buf; a tile past the last step reads nothing
+  // (first row N: its slot fills with zeros and no wave computes it).
+  auto load_step = [&](int qh, int qi0, int buf, int si) {
+    if constexpr (QS == 1) {
+      const size_t qoff = (size_t)qh * N * D;
+      step_loader.load(Q + qoff, N, qi0, opaque_lds(Qs[buf]), wave);
+      step_loader.load(dO + qoff, N, qi0, opaque_lds(dOs[buf]), wave);
+      const uint32_t bytes = (uint32_t)(N - qi0) * 4u;
+      lraw = buffer_load_f32(LSE + (size_t)qh * N + qi0, bytes, 4u * l32);
+      draw = buffer_load_f32(drow + (size_t)qh * N + qi0, bytes, 4u * l32);
+      return;
+    }
+#pragma unroll
+    for (int tq = 0; tq < QS; ++tq) {
+      if (tq > 0) advance(qh, qi0);
+      const bool ok = QS == 1 || si + tq < nsteps;
+      const int h = ok ? qh : qh0, r0 = ok ? qi0 : N;
+      const size_t qoff = (size_t)h * N * D;
+      // The direct loads name their ring slot through an opaque LDS address.
+      // Loads into a slot the compiler can trace (the Qs / dOs arrays) make it
+      // wait for them before every later read of the same array, including
+      // the reads of the other slot, which is this step's: the next step's
+      // tiles would have to arrive before this step could start.  The slots
+      // are ordered by the wait and the barrier that end every step instead.
+      step_loader.load(Q + qoff, N, r0, opaque_lds(Qs[buf] + tq * BQ * D), wave);
+      step_loader.load(dO + qoff, N, r0, opaque_lds(dOs[buf] + tq * BQ * D), wave);
+      // Rows r0 + l32 of the head's L and D (for this wave's own step)
+      // through a buffer descriptor of the rows from r0 on: rows past the end
+      // read as zero (their probabilities are masked), and no lane holds a
+      // 64-bit address.  Every lane loads (no branch around loads); the
+      // values are used only when stored at the end of the step, so nothing
+      // waits for them before.
+      if (tq == qp) {
+        const uint32_t bytes = (uint32_t)(N - r0) * 4u;
+        lraw = buffer_load_f32(LSE + (size_t)h * N + r0, bytes, 4u * l32);
+        draw = buffer_load_f32(drow + (size_t)h * N + r0, bytes, 4u * l32);
+      }
+    }
   };
   auto store_step = [&](int buf) {
-    if (tid < BQ) {
-      Ls[buf][tid] = lraw * 1.4426950408889634f;
-      Ds[buf][tid] = draw;
+    if constexpr (QS == 1) {
+      if (tid < BQ) {
+        Ls[buf][tid] = lraw * 1.4426950408889634f;
+        Ds[buf][tid] = draw;
+      }
+    } else if (kw == 0 && lane < BQ) {
+      Ls[buf][qp * BQ + lane] = lraw * 1.4426950408889634f;
+      Ds[buf][qp * BQ + lane] = draw;
     }
   };
   static_assert(SPW_Q >= 1, "each wave loads part of every tile");
 
-  int ld_h = qh0, ld_q = qstart;  // step being loaded
-  int cu_h = qh0, cu_q = qstart;  // step being computed
-  load_step(ld_h, ld_q, 0);
+  const int nss = (nsteps + QS - 1) / QS;  // steps of the ring (QS query steps each)
+  int ld_h = qh0, ld_q = qstart;  // first query step being loaded
+  int cu_h = qh0, cu_q = qstart;  // first query step being computed
+  load_step(ld_h, ld_q, 0, 0);
   store_step(0);
   wait_counts<FA_VMCNT_LGKM0(0)>();  // this wave's direct loads (K tile included) have landed
   __syncthreads();
 
-  for (int it = 0; it < nsteps; ++it) {
-    const int qi0 = cu_q, buf = it & 1;
-    if (it + 1 < nsteps) {  // into the buffer the previous step read
-      advance(ld_h, ld_q);
-      load_step(ld_h, ld_q, buf ^ 1);
+  for (int it = 0; it < nss; ++it) {
+    int qi0 = cu_q;
+    const int buf = it & 1;
+    if constexpr (QS == 2) {
+      int h1 = cu_h;
+      if (qp == 1) advance(h1, qi0);
+      (void)h1;
     }
+    if (it + 1 < nss) {  // into the buffer the previous step read
+#pragma unroll
+      for (int tq = 0; tq < QS; ++tq) advance(ld_h, ld_q);
+      load_step(ld_h, ld_q, buf ^ 1, QS * (it + 1));
+    }
+    // (QS = 2: a wave whose step is past the last one computes nothing.)
+    if (QS == 1 || QS * it + qp < nsteps) {
 
     // This step's buffer: tiles are 32 D * 2 bytes apart, above every in-tile
     // offset, so adding the buffer offset commutes with the XORs.  The empty
     // asm makes the bases opaque, so the XORs stay in the loop rather than
     // being hoisted into sixteen loop-invariant registers.
-    uint32_t rbs = rb + buf * (BQ * D * 2), tbs = tb + buf * (BQ * D * 2), kws = kwb;
+    uint32_t rbs = rb + buf * (QS * BQ * D * 2) + qp * (BQ * D * 2),
+             tbs = tb + buf * (QS * BQ * D * 2) + qp * (BQ * D * 2), kws = kwb;
     asm volatile("" : "+v"(rbs), "+v"(tbs), "+v"(kws));
     // Visibility: query qi0 + ql sees key mykey iff ql >= mykey - qi0 (causal),
     // the query exists (ql < N - qi0) and the key exists.
@@ -268,7 +314,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
     float pv[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][8 * g + 4 * hh]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][qp * BQ + 8 * g + 4 * hh]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) pv[4 * g + e] = fast_exp2(__builtin_fmaf(sa[4 * g + e], c, -l4[e]));
     }
@@ -308,7 +354,8 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
       }
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][16 * hf + 8 * g2 + 4 * hh]);
+        const f32x4 d4 =
+            *reinterpret_cast<const f32x4*>(&Ds[buf][qp * BQ + 16 * hf + 8 * g2 + 4 * hh]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dsv[4 * g2 + e] = pr[4 * g2 + e] * (dp[8 * hf + 4 * g2 + e] - d4[e]);
       }
@@ -325,10 +372,39 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
         dkacc[nb] = mfma32x32x16(dsA[kc], __builtin_bit_cast(v8, cq), dkacc[nb]);
       }
 
-    if (it + 1 < nsteps) store_step(buf ^ 1);
-    advance(cu_h, cu_q);
+    }
+    if (it + 1 < nss) store_step(buf ^ 1);
+#pragma unroll
+    for (int tq = 0; tq < QS; ++tq) advance(cu_h, cu_q);
     wait_counts<FA_VMCNT_LGKM0(0)>();  // this wave's direct loads have landed
     __syncthreads();
+  }
+
+  if constexpr (QS == 2) {
+    // Merge the two halves of the query steps: the odd-step wave of each key
+    // set leaves its dK and dV accumulators in the Q / dO ring (free after
+    // the last barrier), in its own lane order, and the even-step wave of the
+    // same keys adds them in.
+    static_assert(2 * NB * 16 * 64 * 4 <= (int)sizeof(Qs), "partials fit in the Q ring");
+    float* const xa = reinterpret_cast<float*>(kw == 0 ? &Qs[0][0] : &dOs[0][0]);
+    if (qp == 1) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          xa[(16 * nb + r) * 64 + lane] = dkacc[nb][r];
+          xa[(16 * (NB + nb) + r) * 64 + lane] = dvacc[nb][r];
+        }
+    }
+    __syncthreads();
+    if (qp == 1) return;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dkacc[nb][r] += xa[(16 * nb + r) * 64 + lane];
+        dvacc[nb][r] += xa[(16 * (NB + nb) + r) * 64 + lane];
+      }
   }
 
   // Write dK = scale * sum dS^T Q and dV = sum P^T dO for this wave's keys,
@@ -337,7 +413,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 2) void bwd_kv_kernel(
   // own 32 rows of the K tile (free after the last step's barrier), every
   // store instruction writes whole rows, 1 KiB contiguous.  dK first, then dV
   // through the same rows.
-  T* const stage = Ks + 32 * D * wave;
+  T* const stage = Ks + 32 * D * kw;
   constexpr int LPR = D / 8;    // lanes per row (16 bytes each)
   constexpr int RPI = 64 / LPR;  // rows per store instruction
 #pragma unroll
@@ -611,6 +687,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(
 // B2 H16 H_kv8 N8192 (1024) 1.761 -> 1.697, B4 H32 H_kv8 N4096 (1024) 1.823
 // -> 1.761, B8 H32 H_kv8 N2048 (2048) 0.9832 -> 0.9678.
 constexpr long BWD_SIDE_MAX_BLOCKS = 512;
+// At most 128 blocks of 64 keys (half the CUs): blocks of 64 keys whose two
+// pairs of waves split the query steps, one workgroup per CU, with the other
+// CUs free for the dQ pass beside them.  Measured against 128-key blocks,
+// interleaved on one box (causal, d = 128): B1 H4 N2048 0.0848 -> 0.0744
+// ms, non-causal 0.0896 -> 0.0766, B1 H2 N4096 0.1464 -> 0.1283, B1 H1
+// N8192 0.2742 -> 0.2360, B2 H4 N1024 0.0554 -> 0.0495, B1 H8 H_kv2 N2048
+// 0.2804 -> 0.2368.  At 256 blocks the dK/dV workgroups take every CU and
+// the dQ ones no longer fit beside them: B1 H8 N2048 0.0887 -> 0.0910, B1
+// H4 N4096 0.1536 -> 0.2051.
+constexpr long BWD_Q_SPLIT_MAX = 128;  // blocks of 64 keys
 
 namespace {
 // The second stream and the fork / join events of one device, created on
@@ -674,7 +760,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
 
   const int group = a.H / a.Hkv;
   const int window = WIN ? a.window : 0;
-  const int nkb = (a.N + KV_BK - 1) / KV_BK;
+  // Tiny grids: blocks of 64 keys whose two pairs of waves split the query
+  // steps (QS = 2).
+  const bool qsplit = (long)a.B * a.Hkv * ((a.N + 63) / 64) <= BWD_Q_SPLIT_MAX;
+  const int bk = qsplit ? KV_BK / 2 : KV_BK;
+  const int nkb = (a.N + bk - 1) / bk;
   const int kv_total = a.B * a.Hkv * nkb;
 
   std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
@@ -687,9 +777,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
       if ((e = hipStreamWaitEvent(side->s2, side->fork, 0)) != hipSuccess) return e;
     }
   }
-  e = launch_kernel(bwd_kv_kernel<T, D, CAUSAL, WIN>, dim3(kv_total), dim3(KV_WAVES * 64), s, q, k,
-                    v, dout, a.lse, a.drow, static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.N, nkb,
-                    kv_total, group, window, a.scale, c);
+  if (qsplit)
+    e = launch_kernel(bwd_kv_kernel<T, D, CAUSAL, WIN, 2>, dim3(kv_total), dim3(KV_WAVES * 64), s,
+                      q, k, v, dout, a.lse, a.drow, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
+                      a.N, nkb, kv_total, group, window, a.scale, c);
+  else
+    e = launch_kernel(bwd_kv_kernel<T, D, CAUSAL, WIN, 1>, dim3(kv_total), dim3(KV_WAVES * 64), s,
+                      q, k, v, dout, a.lse, a.drow, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
+                      a.N, nkb, kv_total, group, window, a.scale, c);
   if (e != hipSuccess) return e;
 
   // dQ: four-wave workgroups, two per CU, below one 256-row block per CU and

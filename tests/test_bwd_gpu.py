@@ -108,3 +108,32 @@ def test_bwd_deterministic(causal):
         again = run_fwd_bwd(q, k, v, do, scale, causal)
         for name, a, b in zip(("dQ", "dK", "dV"), first, again):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name} differs between runs"
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,causal,d,dtype", [
+    (1, 2, 2, 4096, True, 128, torch.bfloat16),    # 128 blocks of 64 keys: query steps split
+    (1, 2, 2, 4160, False, 128, torch.bfloat16),   # 130 blocks: 128-key blocks
+    (1, 8, 2, 2048, True, 128, torch.bfloat16),    # grouped heads, split
+    (1, 3, 3, 1111, False, 64, torch.float16),     # ragged end, odd step counts, split
+], ids=["split-128", "nosplit-130", "grouped-split", "f16-d64-ragged-split"])
+def test_bwd_query_split_boundary(B, H, Hkv, N, causal, d, dtype):
+    """Grids of at most 128 blocks of 64 keys run the dK/dV pass with two pairs of waves per
+    block that take the even and the odd query steps and merge dK, dV at the end.  Every
+    key/value group against the oracle, whole tensor and every 32-row block."""
+    seed = 8600 + N + H + Hkv + d + (1 if causal else 0)
+    announce(f"bwd query split B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal} {dtype} seed={seed}")
+    q, k, v, do = attention_inputs(B, H, N, d, dtype, seed, "cpu", with_dout=True, Hkv=Hkv)
+    scale = d ** -0.5
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = fa.attention_fwd(qd, kd, vd, scale, causal)
+    dq, dk, dv = fa.attention_bwd(qd, kd, vd, o, lse, dod, scale, causal)
+    torch.cuda.synchronize()
+    dq_h, dk_h, dv_h = host64(dq), host64(dk), host64(dv)
+    g = H // Hkv
+    for hk in range(Hkv):
+        hs = slice(g * hk, g * hk + g)
+        ref = oracle.attn_bwd(q[0, hs], k[0, hk:hk + 1], v[0, hk:hk + 1], do[0, hs], scale, causal)
+        for name, gt, r in (("dQ", dq_h[0, hs], ref[0]), ("dK", dk_h[0, hk:hk + 1], ref[1]),
+                            ("dV", dv_h[0, hk:hk + 1], ref[2])):
+            check_rel_norm(gt, r, dtype, f"{name} group {hk}")
+            check_rel_norm_blocks(gt, r, dtype, f"{name} group {hk}")
