@@ -92,12 +92,13 @@ __global__ __launch_bounds__(KV_WAVES * 64, QS == 1 ? 2 : 1) void bwd_kv_kernel(
     float scale, float c) {
   using v8 = typename Vec<T>::v8;
   if constexpr (!WIN) window = 0;  // window code only in the WIN instantiation
-  // QS = 2 splits the query steps inside the workgroup (tiny grids): waves w
-  // and w + 2 own the same 32 keys and take the even and the odd query step
-  // of each pair, then merge their dK and dV at the end; a block has 64 keys.
-  // Its Q / dO ring holds two query tiles per step (81 KiB of LDS at
-  // d = 128), so one such workgroup runs per CU, with registers to match.
-  static_assert(QS == 1 || QS == 2, "query steps split in two at most");
+  // QS > 1 splits the query steps inside the workgroup (tiny grids): the
+  // QS waves that own the same 32 keys take every QS-th query step each
+  // (QS = 2: waves w and w + 2, even and odd steps, 64 keys per block; QS =
+  // 4: all four waves, 32 keys), then merge their dK and dV at the end.  The
+  // Q / dO ring holds QS query tiles per step (81 / 138 KiB of LDS at d =
+  // 128), so one such workgroup runs per CU, with registers to match.
+  static_assert(QS == 1 || QS == 2 || QS == 4, "query steps split in 1, 2 or 4");
   constexpr int KWAVES = KV_WAVES / QS;  // waves per set of the block's keys
   constexpr int BK = 32 * KWAVES, BQ = KV_BQ, NB = D / 32;
   constexpr int SPW_Q = BQ * D * 2 / 1024 / KV_WAVES;  // load segments per wave per Q tile
@@ -238,9 +239,9 @@ __global__ __launch_bounds__(KV_WAVES * 64, QS == 1 ? 2 : 1) void bwd_kv_kernel(
   for (int it = 0; it < nss; ++it) {
     int qi0 = cu_q;
     const int buf = it & 1;
-    if constexpr (QS == 2) {
+    if constexpr (QS > 1) {  // this wave's step: qp steps after the pair's (group's) first
       int h1 = cu_h;
-      if (qp == 1) advance(h1, qi0);
+      for (int tq = 0; tq < qp; ++tq) advance(h1, qi0);
       (void)h1;
     }
     if (it + 1 < nss) {  // into the buffer the previous step read
@@ -380,14 +381,21 @@ __global__ __launch_bounds__(KV_WAVES * 64, QS == 1 ? 2 : 1) void bwd_kv_kernel(
     __syncthreads();
   }
 
-  if constexpr (QS == 2) {
-    // Merge the two halves of the query steps: the odd-step wave of each key
-    // set leaves its dK and dV accumulators in the Q / dO ring (free after
-    // the last barrier), in its own lane order, and the even-step wave of the
-    // same keys adds them in.
-    static_assert(2 * NB * 16 * 64 * 4 <= (int)sizeof(Qs), "partials fit in the Q ring");
-    float* const xa = reinterpret_cast<float*>(kw == 0 ? &Qs[0][0] : &dOs[0][0]);
-    if (qp == 1) {
+  if constexpr (QS > 1) {
+    // Merge the parts of the query steps: each wave with qp > 0 leaves its
+    // dK and dV accumulators in a region of the Q / dO ring (free after the
+    // last barrier), in its own lane order, and the qp = 0 wave of the same
+    // keys adds them in, in qp order.
+    constexpr int RF = 2 * NB * 16 * 64;                    // floats per region
+    constexpr int RPA = (int)sizeof(Qs) / (RF * 4);          // regions per array
+    static_assert(RPA >= 1 && 2 * RPA >= (QS - 1) * KWAVES, "partials fit in the ring");
+    auto region = [&](int p) {  // region of the wave (key set kw, step part p)
+      const int ri = (p - 1) * KWAVES + kw;
+      return ri < RPA ? reinterpret_cast<float*>(&Qs[0][0]) + ri * RF
+                      : reinterpret_cast<float*>(&dOs[0][0]) + (ri - RPA) * RF;
+    };
+    if (qp > 0) {
+      float* const xa = region(qp);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -397,14 +405,17 @@ __global__ __launch_bounds__(KV_WAVES * 64, QS == 1 ? 2 : 1) void bwd_kv_kernel(
         }
     }
     __syncthreads();
-    if (qp == 1) return;
+    if (qp > 0) return;
+    for (int p = 1; p < QS; ++p) {
+      const float* const xa = region(p);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dkacc[nb][r] += xa[(16 * nb + r) * 64 + lane];
-        dvacc[nb][r] += xa[(16 * (NB + nb) + r) * 64 + lane];
-      }
+        for (int r = 0; r < 16; ++r) {
+          dkacc[nb][r] += xa[(16 * nb + r) * 64 + lane];
+          dvacc[nb][r] += xa[(16 * (NB + nb) + r) * 64 + lane];
+        }
+    }
   }
 
   // Write dK = scale * sum dS^T Q and dV = sum P^T dO for this wave's keys,
@@ -695,8 +706,13 @@ constexpr long BWD_SIDE_MAX_BLOCKS = 512;
 // N8192 0.2742 -> 0.2360, B2 H4 N1024 0.0554 -> 0.0495, B1 H8 H_kv2 N2048
 // 0.2804 -> 0.2368.  At 256 blocks the dK/dV workgroups take every CU and
 // the dQ ones no longer fit beside them: B1 H8 N2048 0.0887 -> 0.0910, B1
-// H4 N4096 0.1536 -> 0.2051.
-constexpr long BWD_Q_SPLIT_MAX = 128;  // blocks of 64 keys
+// H4 N4096 0.1536 -> 0.2051.  Where even 32-key blocks number at most 128,
+// four waves own each block's keys and take every fourth step, against the
+// two-way split: grouped B1 H8 H_kv2 N2048 0.2396 -> 0.1506, B1 H16 H_kv2
+// N2048 0.4609 -> 0.2787, B1 H8 H_kv1 N4096 0.8974 -> 0.5287; B1 H1 N4096
+// 0.1282 -> 0.1066, B1 H2 N2048 0.0738 -> 0.0677, B1 H4 N1024 0.0480 ->
+// 0.0491.
+constexpr long BWD_Q_SPLIT_MAX = 128;  // blocks (of 64, or of 32, keys)
 
 namespace {
 // The second stream and the fork / join events of one device, created on
@@ -760,10 +776,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
 
   const int group = a.H / a.Hkv;
   const int window = WIN ? a.window : 0;
-  // Tiny grids: blocks of 64 keys whose two pairs of waves split the query
-  // steps (QS = 2).
-  const bool qsplit = (long)a.B * a.Hkv * ((a.N + 63) / 64) <= BWD_Q_SPLIT_MAX;
-  const int bk = qsplit ? KV_BK / 2 : KV_BK;
+  // Tiny grids: blocks of 64 (32) keys whose waves split the query steps in
+  // two (four).
+  const long kvh = (long)a.B * a.Hkv;
+  const int qs = kvh * ((a.N + 31) / 32) <= BWD_Q_SPLIT_MAX ? 4
+                 : kvh * ((a.N + 63) / 64) <= BWD_Q_SPLIT_MAX ? 2 : 1;
+  const int bk = KV_BK / qs;
   const int nkb = (a.N + bk - 1) / bk;
   const int kv_total = a.B * a.Hkv * nkb;
 
@@ -777,7 +795,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
       if ((e = hipStreamWaitEvent(side->s2, side->fork, 0)) != hipSuccess) return e;
     }
   }
-  if (qsplit)
+  if (qs == 4)
+    e = launch_kernel(bwd_kv_kernel<T, D, CAUSAL, WIN, 4>, dim3(kv_total), dim3(KV_WAVES * 64), s,
+                      q, k, v, dout, a.lse, a.drow, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
+                      a.N, nkb, kv_total, group, window, a.scale, c);
+  else if (qs == 2)
     e = launch_kernel(bwd_kv_kernel<T, D, CAUSAL, WIN, 2>, dim3(kv_total), dim3(KV_WAVES * 64), s,
                       q, k, v, dout, a.lse, a.drow, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
                       a.N, nkb, kv_total, group, window, a.scale, c);

@@ -111,15 +111,20 @@ def test_bwd_deterministic(causal):
 
 
 @pytest.mark.parametrize("B,H,Hkv,N,causal,d,dtype", [
-    (1, 2, 2, 4096, True, 128, torch.bfloat16),    # 128 blocks of 64 keys: query steps split
-    (1, 2, 2, 4160, False, 128, torch.bfloat16),   # 130 blocks: 128-key blocks
-    (1, 8, 2, 2048, True, 128, torch.bfloat16),    # grouped heads, split
-    (1, 3, 3, 1111, False, 64, torch.float16),     # ragged end, odd step counts, split
-], ids=["split-128", "nosplit-130", "grouped-split", "f16-d64-ragged-split"])
+    (1, 2, 2, 4096, True, 128, torch.bfloat16),    # 128 blocks of 64 keys: steps split in 2
+    (1, 2, 2, 4160, False, 128, torch.bfloat16),   # 130 blocks of 64 keys: not split
+    (1, 4, 4, 2048, True, 128, torch.bfloat16),    # 128 blocks of 64, 256 of 32: split in 2
+    (1, 8, 4, 2048, False, 64, torch.float16),     # grouped heads, split in 2
+    (1, 8, 2, 2048, True, 128, torch.bfloat16),    # 128 blocks of 32 keys: split in 4
+    (1, 3, 3, 1111, False, 64, torch.float16),     # ragged end, odd step counts, split in 4
+], ids=["split2-128", "nosplit-130", "split2-small", "split2-grouped", "split4-grouped",
+        "split4-f16-d64-ragged"])
 def test_bwd_query_split_boundary(B, H, Hkv, N, causal, d, dtype):
-    """Grids of at most 128 blocks of 64 keys run the dK/dV pass with two pairs of waves per
-    block that take the even and the odd query steps and merge dK, dV at the end.  Every
-    key/value group against the oracle, whole tensor and every 32-row block."""
+    """Grids of at most 128 blocks of 32 keys run the dK/dV pass with four waves per block of
+    32 keys, each taking every fourth query step; else, grids of at most 128 blocks of 64 keys
+    with two pairs of waves per block taking the even and the odd steps.  The waves merge dK
+    and dV at the end.  Every key/value group against the oracle, whole tensor and every
+    32-row block."""
     seed = 8600 + N + H + Hkv + d + (1 if causal else 0)
     announce(f"bwd query split B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal} {dtype} seed={seed}")
     q, k, v, do = attention_inputs(B, H, N, d, dtype, seed, "cpu", with_dout=True, Hkv=Hkv)
