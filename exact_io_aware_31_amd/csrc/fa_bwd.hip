@@ -12,7 +12,8 @@
 // (D_i equals sum_j P_ij dP_ij because each row of O is P_i V.)
 //
 // Three kernels, none of which uses atomics (every output element is written
-// once, by one lane, so the results are deterministic); on small grids the
+// once, by one lane, and partial sums are added in a fixed order, so the
+// results are deterministic); on small grids and with grouped heads the
 // third runs on a second stream beside the second (see the launchers):
 //   1. bwd_pre: D = rowsum(dO o O) in fp32.
 //   2. bwd_kv:  dK and dV.  One workgroup of 4 waves per block of 128 keys;
@@ -23,7 +24,10 @@
 //      dV += P^T dO and dK += dS^T Q straight from those registers; the B
 //      operands dO and Q come from transpose reads of the row-major tiles.
 //      The kernel fits in 256 registers, so two workgroups share a CU (two
-//      waves per SIMD hide each other's LDS and MFMA latencies).
+//      waves per SIMD hide each other's LDS and MFMA latencies).  On tiny
+//      grids a block has 64 or 32 keys, and the two or four waves that own
+//      the same keys take alternate query steps, then add their dK and dV
+//      through LDS.
 //   3. bwd_dq:  dQ, with the forward pass's shape: one workgroup of 8 waves
 //      per block of 256 query rows, 64-key K and V tiles streaming through a
 //      three-deep LDS ring, and transposed products so that each lane owns
