@@ -717,6 +717,15 @@ constexpr long BWD_SIDE_MAX_BLOCKS = 512;
 // 0.1282 -> 0.1066, B1 H2 N2048 0.0738 -> 0.0677, B1 H4 N1024 0.0480 ->
 // 0.0491.
 constexpr long BWD_Q_SPLIT_MAX = 128;  // blocks (of 64, or of 32, keys)
+// With grouped heads every block walks its whole group, so its walk is long
+// enough for the split to pay on up to 256 blocks, against 128-key blocks
+// (two-way) or the two-way split (four-way): B1 H16 H_kv4 N4096 0.5492 ->
+// 0.4602 ms, B1 H8 H_kv2 N8192 1.0667 -> 0.9599, B2 H16 H_kv4 N2048 0.2847
+// -> 0.2417, B1 H32 H_kv4 N4096 1.0800 -> 0.9043, B1 H32 H_kv8 N2048 0.2848
+// -> 0.2427; four-way at 256 blocks of 32 keys, B1 H16 H_kv4 N2048 0.2397
+// -> 0.1631.
+constexpr long BWD_Q_SPLIT4_MAX_GROUPED = 256;
+constexpr long BWD_Q_SPLIT2_MAX_GROUPED = 256;
 
 namespace {
 // The second stream and the fork / join events of one device, created on
@@ -783,8 +792,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   // Tiny grids: blocks of 64 (32) keys whose waves split the query steps in
   // two (four).
   const long kvh = (long)a.B * a.Hkv;
-  const int qs = kvh * ((a.N + 31) / 32) <= BWD_Q_SPLIT_MAX ? 4
-                 : kvh * ((a.N + 63) / 64) <= BWD_Q_SPLIT_MAX ? 2 : 1;
+  const long max4 = group > 1 ? BWD_Q_SPLIT4_MAX_GROUPED : BWD_Q_SPLIT_MAX;
+  const long max2 = group > 1 ? BWD_Q_SPLIT2_MAX_GROUPED : BWD_Q_SPLIT_MAX;
+  const int qs = kvh * ((a.N + 31) / 32) <= max4 ? 4 : kvh * ((a.N + 63) / 64) <= max2 ? 2 : 1;
   const int bk = KV_BK / qs;
   const int nkb = (a.N + bk - 1) / bk;
   const int kv_total = a.B * a.Hkv * nkb;

@@ -117,14 +117,16 @@ def test_bwd_deterministic(causal):
     (1, 8, 4, 2048, False, 64, torch.float16),     # grouped heads, split in 2
     (1, 8, 2, 2048, True, 128, torch.bfloat16),    # 128 blocks of 32 keys: split in 4
     (1, 3, 3, 1111, False, 64, torch.float16),     # ragged end, odd step counts, split in 4
+    (2, 16, 4, 2048, True, 128, torch.bfloat16),   # grouped, 256 blocks of 64 keys: split in 2
+    (1, 16, 4, 2048, True, 128, torch.bfloat16),   # grouped, 256 blocks of 32 keys: split in 4
 ], ids=["split2-128", "nosplit-130", "split2-small", "split2-grouped", "split4-grouped",
-        "split4-f16-d64-ragged"])
+        "split4-f16-d64-ragged", "split2-grouped-256", "split4-grouped-256"])
 def test_bwd_query_split_boundary(B, H, Hkv, N, causal, d, dtype):
-    """Grids of at most 128 blocks of 32 keys run the dK/dV pass with four waves per block of
-    32 keys, each taking every fourth query step; else, grids of at most 128 blocks of 64 keys
-    with two pairs of waves per block taking the even and the odd steps.  The waves merge dK
-    and dV at the end.  Every key/value group against the oracle, whole tensor and every
-    32-row block."""
+    """Grids of at most 128 blocks of 32 keys (256 with grouped heads) run the dK/dV pass with
+    four waves per block of 32 keys, each taking every fourth query step; else, grids of at
+    most 128 blocks of 64 keys (256 with grouped heads) with two pairs of waves per block taking
+    the even and the odd steps.  The waves merge dK and dV at the end.  Key/value groups
+    against the oracle (at most three per case), whole tensor and every 32-row block."""
     seed = 8600 + N + H + Hkv + d + (1 if causal else 0)
     announce(f"bwd query split B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal} {dtype} seed={seed}")
     q, k, v, do = attention_inputs(B, H, N, d, dtype, seed, "cpu", with_dout=True, Hkv=Hkv)
@@ -135,10 +137,11 @@ def test_bwd_query_split_boundary(B, H, Hkv, N, causal, d, dtype):
     torch.cuda.synchronize()
     dq_h, dk_h, dv_h = host64(dq), host64(dk), host64(dv)
     g = H // Hkv
-    for hk in range(Hkv):
+    groups = sorted({(0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 2)})
+    for b, hk in groups:
         hs = slice(g * hk, g * hk + g)
-        ref = oracle.attn_bwd(q[0, hs], k[0, hk:hk + 1], v[0, hk:hk + 1], do[0, hs], scale, causal)
-        for name, gt, r in (("dQ", dq_h[0, hs], ref[0]), ("dK", dk_h[0, hk:hk + 1], ref[1]),
-                            ("dV", dv_h[0, hk:hk + 1], ref[2])):
-            check_rel_norm(gt, r, dtype, f"{name} group {hk}")
-            check_rel_norm_blocks(gt, r, dtype, f"{name} group {hk}")
+        ref = oracle.attn_bwd(q[b, hs], k[b, hk:hk + 1], v[b, hk:hk + 1], do[b, hs], scale, causal)
+        for name, gt, r in (("dQ", dq_h[b, hs], ref[0]), ("dK", dk_h[b, hk:hk + 1], ref[1]),
+                            ("dV", dv_h[b, hk:hk + 1], ref[2])):
+            check_rel_norm(gt, r, dtype, f"{name} group ({b},{hk})")
+            check_rel_norm_blocks(gt, r, dtype, f"{name} group ({b},{hk})")
