@@ -793,7 +793,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   // two (four).
   const long kvh = (long)a.B * a.Hkv;
   const long max4 = group > 1 ? BWD_Q_SPLIT4_MAX_GROUPED : BWD_Q_SPLIT_MAX;
-  const long max2 = group > 1 ? BWD_Q_SPLIT2_MAX_GROUPED : BWD_Q_SPLIT_MAX;
+  // (At d = 64 the two-way split workgroup needs half the LDS and fewer
+  // registers, so a dQ workgroup still fits beside it: B1 H2 N8192 0.2061
+  // -> 0.1812 ms, B1 H4 N4096 0.1140 -> 0.1079, B1 H8 N2048 0.0700 ->
+  // 0.0688, non-causal 0.0671 -> 0.0679, at 256 blocks.)
+  const long max2 = (group > 1 || D == 64) ? BWD_Q_SPLIT2_MAX_GROUPED : BWD_Q_SPLIT_MAX;
   const int qs = kvh * ((a.N + 31) / 32) <= max4 ? 4 : kvh * ((a.N + 63) / 64) <= max2 ? 2 : 1;
   const int bk = KV_BK / qs;
   const int nkb = (a.N + bk - 1) / bk;

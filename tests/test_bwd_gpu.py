@@ -119,14 +119,15 @@ def test_bwd_deterministic(causal):
     (1, 3, 3, 1111, False, 64, torch.float16),     # ragged end, odd step counts, split in 4
     (2, 16, 4, 2048, True, 128, torch.bfloat16),   # grouped, 256 blocks of 64 keys: split in 2
     (1, 16, 4, 2048, True, 128, torch.bfloat16),   # grouped, 256 blocks of 32 keys: split in 4
+    (1, 4, 4, 4096, True, 64, torch.bfloat16),     # d = 64, 256 blocks of 64 keys: split in 2
 ], ids=["split2-128", "nosplit-130", "split2-small", "split2-grouped", "split4-grouped",
-        "split4-f16-d64-ragged", "split2-grouped-256", "split4-grouped-256"])
+        "split4-f16-d64-ragged", "split2-grouped-256", "split4-grouped-256", "split2-d64-256"])
 def test_bwd_query_split_boundary(B, H, Hkv, N, causal, d, dtype):
     """Grids of at most 128 blocks of 32 keys (256 with grouped heads) run the dK/dV pass with
     four waves per block of 32 keys, each taking every fourth query step; else, grids of at
-    most 128 blocks of 64 keys (256 with grouped heads) with two pairs of waves per block taking
-    the even and the odd steps.  The waves merge dK and dV at the end.  Key/value groups
-    against the oracle (at most three per case), whole tensor and every 32-row block."""
+    most 128 blocks of 64 keys (256 with grouped heads or d = 64) with two pairs of waves per
+    block taking the even and the odd steps.  The waves merge dK and dV at the end.  Key/value
+    groups against the oracle (at most three per case), whole tensor and every 32-row block."""
     seed = 8600 + N + H + Hkv + d + (1 if causal else 0)
     announce(f"bwd query split B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal} {dtype} seed={seed}")
     q, k, v, do = attention_inputs(B, H, N, d, dtype, seed, "cpu", with_dout=True, Hkv=Hkv)
