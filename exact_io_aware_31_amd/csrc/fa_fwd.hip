@@ -471,13 +471,17 @@ constexpr int FWD_SMALL_WINDOW = 2048;
 // H1 N256 0.0086 / 0.0088.  Past 256 blocks it mostly loses (a second round
 // of workgroups): B1 H16 N4096 0.0827 -> 0.1126, B1 H4 N8192 0.1263 ->
 // 0.1440, B1 H32 N1024 0.0210 -> 0.0233; non-causal B1 H16 N2048 0.0379 ->
-// 0.0548.  A window keeps the other shapes.
+// 0.0548.  A window keeps the other shapes.  At d = 64 the ring takes 64
+// KiB, two such workgroups fit on a CU, and the split runs up to 512 blocks:
+// B1 H16 N2048 0.0274 -> 0.0208 ms, B1 H8 N4096 0.0472 -> 0.0340, B1 H4
+// N8192 0.0878 -> 0.0652, B1 H32 N1024 0.0151 -> 0.0116, non-causal B1 H16
+// N2048 0.0268 -> 0.0261.
 constexpr long FWD_KEY_SPLIT_MAX = 256;
 
 template <typename T, int D, bool CAUSAL, bool WIN>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   if constexpr (!WIN) {
-    if ((long)a.B * a.H * ((a.N + 63) / 64) <= FWD_KEY_SPLIT_MAX)
+    if ((long)a.B * a.H * ((a.N + 63) / 64) <= (D == 64 ? 2 : 1) * FWD_KEY_SPLIT_MAX)
       return launch_fwd_nw<T, D, CAUSAL, WIN, 4, 2>(a, s);
   }
   const long blocks256 = (long)a.B * a.H * ((a.N + 255) / 256);

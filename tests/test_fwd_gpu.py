@@ -117,13 +117,15 @@ def test_fwd_both_workgroup_shapes(H, causal, d, dtype):
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float16, 64)],
                          ids=["bf16-d128", "f16-d64"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-@pytest.mark.parametrize("H,N", [(4, 4096), (4, 4097), (2, 4000)],
-                         ids=["keysplit-256", "4wave-260", "keysplit-odd-tiles"])
+@pytest.mark.parametrize("H,N", [(4, 4096), (4, 4097), (2, 4000), (8, 4096), (8, 4097)],
+                         ids=["keysplit-256", "4wave-260", "keysplit-odd-tiles", "512",
+                              "520"])
 def test_fwd_key_split_boundary(H, N, causal, d, dtype):
-    """Grids of at most 256 blocks of 64 rows run four-wave workgroups whose two pairs of waves
-    split each step's keys and merge at the end: B1 H4 N4096 is 256 such blocks, N4097 is 260
-    and runs the plain four-wave shape; N4000 leaves an odd number of key tiles, so the last
-    step's second tile starts past the end.  Every head against the oracle."""
+    """Grids of at most 256 blocks of 64 rows (512 at d = 64) run four-wave workgroups whose
+    two pairs of waves split each step's keys and merge at the end: B1 H4 N4096 is 256 such
+    blocks, N4097 is 260 and runs the plain four-wave shape; N4000 leaves an odd number of key
+    tiles, so the last step's second tile starts past the end; B1 H8 N4096 (512 blocks) splits
+    at d = 64 only, N4097 (520) at neither.  Every head against the oracle."""
     B = 1
     seed = 7400 + H + N + d + (1 if causal else 0)
     announce(f"fwd key split B{B} H{H} N{N} d{d} causal={causal} {dtype} seed={seed}")

@@ -80,12 +80,12 @@ def run_fwd(q, k, v, scale, causal, window):
 
 # (mask, workgroup shape) -> (B, H, N, window): without a window, the launcher takes four-wave
 # workgroups of 64 rows that split each step's keys between two pairs of waves for at most 256
-# blocks of 64 rows; four-wave workgroups of 128 rows for at most 256 blocks of 256 query rows,
+# blocks of 64 rows (512 at d = 64); four-wave workgroups of 128 rows for at most 256 blocks of 256 query rows,
 # for N <= 2048 up to 1024 blocks, and for any window of up to 2048 keys; eight-wave ones
 # otherwise.
-SHAPES = {("full", "keysplit"): (1, 2, 512, 0), ("full", "4wave"): (1, 40, 512, 0),
+SHAPES = {("full", "keysplit"): (1, 2, 512, 0), ("full", "4wave"): (1, 80, 512, 0),
           ("full", "8wave"): (2, 264, 512, 0),
-          ("causal", "keysplit"): (1, 2, 512, 0), ("causal", "4wave"): (1, 40, 512, 0),
+          ("causal", "keysplit"): (1, 2, 512, 0), ("causal", "4wave"): (1, 80, 512, 0),
           ("causal", "8wave"): (2, 264, 512, 0),
           ("window", "4wave"): (1, 2, 1024, 300), ("window", "8wave"): (1, 64, 4096, 2500)}
 
